@@ -1,0 +1,230 @@
+"""Pins for the oracle's bf16, RoPE, INT8 and window functions (CPU only).
+
+Each test ties an oracle function to something other than itself: a
+hand-worked fixture, a library special case, a closed form or an invariant.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ bf16 ----
+
+def test_bf16_hand_cases():
+    for xs, ys in _golden("bf16_rounding_cases.json")["cases"]:
+        env = {"__builtins__": {}, "inf": math.inf}
+        x, y = eval(xs, env), eval(ys, env)  # fixture expressions are plain arithmetic
+        got = oracle.round_to_bf16(np.array([x]))[0]
+        assert got == y, (xs, got, y)
+
+
+def test_bf16_matches_torch_on_fp32_inputs():
+    # library special case: torch's float32 -> bfloat16 cast rounds to nearest
+    # even; on fp32 inputs the oracle must agree bit for bit.
+    rng = np.random.default_rng(7)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(50000) * 1e-38).astype(np.float32),   # subnormal range
+        (rng.standard_normal(50000) * 1e30).astype(np.float32),
+    ])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.f64_to_bf16_bits(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    back = oracle.bf16_bits_to_f64(got)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
+def test_input_rounding_agrees_with_oracle_rounding():
+    # the generator's bit trick and the oracle's definition are separate code;
+    # they must agree on fp32 draws
+    d = np.random.default_rng(3).standard_normal(100000).astype(np.float32)
+    assert np.array_equal(workloads.f32_to_bf16_bits(d), oracle.f64_to_bf16_bits(d.astype(np.float64)))
+
+
+# ------------------------------------------------------------------ RoPE ----
+
+def test_rope_frequencies_closed_form():
+    # theta = 256 and a 16-wide temporal slice give theta**(-2i/16) = 2**-i
+    f = oracle.rope_frequencies(16, 256.0)
+    assert np.array_equal(f, 2.0 ** -np.arange(8))
+    g = oracle.rope_frequencies(56, 256.0)
+    assert np.allclose(g, 2.0 ** (-2.0 * np.arange(28) / 7.0), rtol=0, atol=1e-16)
+
+
+def test_rope_pos_zero_is_identity():
+    x = np.random.default_rng(0).standard_normal((5, 3, 128))
+    assert np.array_equal(oracle.rope3d(x, np.zeros((5, 3), np.int32)), x)
+
+
+def test_rope_matches_complex_multiplication():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((40, 2, 128))
+    pos = rng.integers(0, 400, size=(40, 3))
+    y = oracle.rope3d(x, pos)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    ang = np.concatenate([
+        pos[:, 0:1] * 256.0 ** (-np.arange(8) / 8.0),
+        pos[:, 1:2] * 256.0 ** (-np.arange(28) / 28.0),
+        pos[:, 2:3] * 256.0 ** (-np.arange(28) / 28.0)], axis=1)
+    w = z * np.exp(1j * ang)[:, None, :]
+    assert np.max(np.abs(y[..., 0::2] - w.real)) < 1e-12
+    assert np.max(np.abs(y[..., 1::2] - w.imag)) < 1e-12
+
+
+def test_rope_preserves_pair_norms_and_axis_slices():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((30, 4, 128))
+    pos = rng.integers(0, 300, size=(30, 3))
+    y = oracle.rope3d(x, pos)
+    assert np.allclose(np.hypot(y[..., 0::2], y[..., 1::2]),
+                       np.hypot(x[..., 0::2], x[..., 1::2]), atol=1e-12)
+    # moving only h touches only dims 16..71
+    p2 = pos.copy()
+    p2[:, 1] += 5
+    y2 = oracle.rope3d(x, p2)
+    diff = np.any(y2 != y, axis=(0, 1))
+    assert not diff[:16].any() and diff[16:72].all() and not diff[72:].any()
+
+
+def test_rope_scores_depend_only_on_position_differences():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((20, 2, 128))
+    k = rng.standard_normal((25, 2, 128))
+    pq = rng.integers(0, 50, size=(20, 3))
+    pk = rng.integers(0, 50, size=(25, 3))
+    shift = np.array([37, -3, 11])
+    s0 = np.einsum("ihd,jhd->hij", oracle.rope3d(q, pq), oracle.rope3d(k, pk))
+    s1 = np.einsum("ihd,jhd->hij", oracle.rope3d(q, pq + shift), oracle.rope3d(k, pk + shift))
+    assert np.max(np.abs(s0 - s1)) < 1e-11
+
+
+def test_rope_bf16_is_exact_rotation_rounded_once():
+    cfg = workloads.ALL["c0"]
+    inp = workloads.make_inputs(cfg)
+    kv = inp.k[inp.video_rows]
+    y = oracle.rope3d_bf16(kv, inp.pos)
+    exact = oracle.rope3d(oracle.bf16_bits_to_f64(kv), inp.pos)
+    # each output is a bf16 value within half a bf16 ulp of the exact rotation
+    assert np.array_equal(y, oracle.round_to_bf16(y))
+    ulp = np.ldexp(1.0, np.frexp(np.abs(exact))[1] - 8)
+    assert np.all(np.abs(y - exact) <= 0.5 * ulp + 1e-300)
+
+
+# ------------------------------------------------------------------ INT8 ----
+
+def test_quant_hand_example():
+    g = _golden("quant_hand_example.json")
+    x = np.array([g["x_head"] + [0.0] * (128 - len(g["x_head"]))])
+    codes, scale = oracle.quantise_int8(x)
+    assert scale[0] == np.float32(g["scale"])
+    assert list(codes[0, :len(g["codes_head"])]) == g["codes_head"]
+    assert not codes[0, len(g["codes_head"]):].any()
+    c0, s0 = oracle.quantise_int8(np.zeros((1, 128)))
+    assert s0[0] == g["x_zero_row_scale"] and not c0.any()
+
+
+def _bf16_rows(n, seed, spread=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 128)).astype(np.float32)
+    if spread:
+        x *= (2.0 ** rng.integers(-20, 20, size=(n, 1))).astype(np.float32)
+    return oracle.bf16_bits_to_f64(workloads.f32_to_bf16_bits(x))
+
+
+def test_quant_matches_torch_fp32_division():
+    # the float64-then-round emulation must equal IEEE fp32 division done by
+    # another library (torch float32 tensors)
+    x = _bf16_rows(4000, 5)
+    codes, scale = oracle.quantise_int8(x)
+    xt = torch.from_numpy(x.astype(np.float32))
+    a = xt.abs().amax(dim=1)
+    st = a / torch.tensor(127.0, dtype=torch.float32)
+    assert np.array_equal(st.numpy(), scale)
+    qt = xt / st[:, None]
+    ct = torch.clamp(torch.round(qt), -127, 127).to(torch.int8)   # torch.round: half to even
+    assert np.array_equal(ct.numpy(), codes)
+
+
+def test_quant_roundtrip_bound_and_symmetry():
+    x = _bf16_rows(5000, 6)
+    codes, scale = oracle.quantise_int8(x)
+    s = scale.astype(np.float64)[:, None]
+    err = np.abs(x - codes.astype(np.float64) * s)
+    assert np.all(err <= s * (0.5 + 2.0 ** -18))
+    amax_idx = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.abs(codes[np.arange(len(x)), amax_idx]) == 127)
+    cn, sn = oracle.quantise_int8(-x)
+    assert np.array_equal(cn, -codes) and np.array_equal(sn, scale)
+    assert codes.min() >= -127
+
+
+def test_quant_ties_round_to_even():
+    # x/scale lands exactly on k + 1/2 when scale is a power of two
+    x = np.zeros((4, 128))
+    x[:, 0] = 127.0 * 2.0 ** -3           # scale = 2**-3 exactly
+    x[0, 1:4] = np.array([0.5, 1.5, 2.5]) * 2.0 ** -3
+    x[1, 1:4] = -np.array([0.5, 1.5, 2.5]) * 2.0 ** -3
+    codes, scale = oracle.quantise_int8(x)
+    assert scale[0] == 2.0 ** -3
+    assert list(codes[0, 1:4]) == [0, 2, 2]
+    assert list(codes[1, 1:4]) == [0, -2, -2]
+
+
+# ---------------------------------------------------------------- window ----
+
+def _window_brute(slot_t, budget):
+    valid = sorted((t, i) for i, t in enumerate(slot_t) if t >= 0)
+    chosen = valid[max(0, len(valid) - budget):] if budget > 0 else []
+    return [i for _, i in chosen]
+
+
+def test_window_brute_force():
+    rng = np.random.default_rng(8)
+    for trial in range(300):
+        n = int(rng.integers(0, 30))
+        ts = rng.permutation(100)[:n]
+        ts[rng.random(n) < 0.3] = -1
+        for b in (0, 1, 3, 18, 40):
+            assert list(oracle.window_select(ts, b)) == _window_brute(list(ts), b)
+
+
+def test_window_errors():
+    with pytest.raises(oracle.WindowError):
+        oracle.window_select([3, 5, 3], 2)
+    with pytest.raises(oracle.WindowError):
+        oracle.window_select([1, 2], -1)
+    assert list(oracle.window_select([-1, -1], 5)) == []
+
+
+# ------------------------------------------------------------ page sizes ----
+
+def test_workload_geometry_matches_pages():
+    g = _golden("page_sizes.json")
+    c4 = workloads.CONFIGS["c4"]
+    assert c4.tokens_per_frame == g["tokens_per_latent_frame_704x1280"]["value"]
+    assert c4.n_heads == g["heads"]["value"]
+    assert workloads.HEAD_DIM == g["head_dim"]["value"]
+    assert workloads.CONFIGS["c2"].window == g["history_budget_frames"]["value"]
+    # 12-s turns at 6 latent frames per second = 72 frames
+    assert c4.segments[0].n_frames == 12 * g["latent_frames_per_second"]["value"]
+    per_tok = 2 * c4.n_heads * workloads.HEAD_DIM   # K and V INT8 codes
+    assert per_tok == g["int8_kv_bytes_per_token_per_layer"]["value"]
+    assert per_tok * g["dit_layers"]["value"] * c4.tokens_per_frame == \
+        g["int8_kv_bytes_per_frame_54_layers"]["value"]
+    assert c4.n_hist_rows == 253440 and c4.n_cur == 63616
