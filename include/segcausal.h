@@ -1,0 +1,217 @@
+/*
+ * segcausal.h -- C ABI of libsegcausal.so: segment-wise causal joint attention
+ * over a persistent per-layer KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method: inside each dual-stream MMDiT block, the current segment's text
+ * and video tokens attend jointly over the layer's KV cache of earlier
+ * segments plus the current segment; video positions carry 3D RoPE; the cache
+ * may be stored in INT8 while attention is computed in BF16; a single-GPU
+ * deployment bounds the history to a window of recent latent frames.
+ * Sources: "Hy-Nomas: Towards Free-Form Interactive World Generation" (model
+ * card), section "Segment-Autoregressive Diffusion Transformer", its
+ * architecture table, and section "Single-GPU Low-Memory Inference";
+ * "Hy-Nomas Explained: How Tencent's Open World Model Runs Steerable Video on
+ * an RTX 4090", Step 2 "Segment-wise causal joint attention".
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are caller-owned DEVICE memory unless marked "host".
+ *    The library never allocates, frees or keeps pointers after returning.
+ *  - bf16 tensors of rows are laid out [rows][heads][128] with the 128 head
+ *    elements contiguous; the token and head strides are given in ELEMENTS and
+ *    must be multiples of 8 (16-byte aligned rows); base pointers must be
+ *    16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call is asynchronous on that stream; the library never
+ *    synchronises. The caller keeps buffers alive until the stream has run the
+ *    work and orders writes and reads of the same memory on its streams.
+ *  - All argument checks happen on the host before anything is launched. On a
+ *    non-zero status nothing has been written; segcausal_last_error() returns
+ *    a message (per calling thread). Device-side bounds (e.g. that a pointer
+ *    really spans the stated sizes) cannot be checked: they are preconditions.
+ *  - No call prints, exits or throws across the ABI. The library holds no
+ *    device state and is reentrant.
+ */
+#ifndef SEGCAUSAL_H
+#define SEGCAUSAL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define SEGC_OK           0
+#define SEGC_EINVAL       1  /* bad argument: null/misaligned pointer, bad size, stride, slot, segment */
+#define SEGC_EUNSUPPORTED 2  /* well-formed but outside what the kernels implement */
+#define SEGC_EHIP         3  /* a HIP launch error; the message has hipGetErrorString */
+
+/* cache element types */
+#define SEGC_BF16 0
+#define SEGC_INT8 1
+
+#define SEGC_HEAD_DIM 128    /* 16 heads x 128 dims per head (model card, architecture table) */
+#define SEGC_MAX_SEG  16     /* packed segments per attention call */
+
+/*
+ * A per-layer KV cache of latent frames ("the layer's KV cache supplying
+ * context from earlier segments", model card, section "Segment-Autoregressive
+ * Diffusion Transformer"). Holds video tokens only, K after RoPE, V as is.
+ *
+ * Memory (all caller-owned device memory):
+ *   k, v       : [n_slots][n_heads][tokens_per_frame][128], bf16 (SEGC_BF16)
+ *                or int8 codes (SEGC_INT8); one slot holds one latent frame,
+ *                its tokens in raster (h, w) order.
+ *   k_scale,
+ *   v_scale    : [n_slots][n_heads][tokens_per_frame] fp32, SEGC_INT8 only
+ *                (NULL for SEGC_BF16). Dequantised value = code * scale.
+ * The host tracks which latent-frame index t each slot holds (see
+ * window_select).
+ */
+typedef struct segc_cache {
+  int32_t dtype;             /* SEGC_BF16 or SEGC_INT8 */
+  int32_t n_heads;
+  int32_t head_dim;          /* must be 128 */
+  int32_t tokens_per_frame;  /* G = grid_h * grid_w, e.g. 22 * 40 = 880 */
+  int32_t n_slots;           /* frame capacity */
+  int32_t reserved;
+  void*  k;
+  void*  v;
+  float* k_scale;
+  float* v_scale;
+} segc_cache;
+
+/*
+ * rope3d_apply -- 3D rotary position embedding of video rows.
+ * Source: model card architecture table, "Position encoding": 3D RoPE with
+ * temporal/height/width dimensions [16, 56, 56] and theta 256; section
+ * "Segment-Autoregressive Diffusion Transformer": RoPE encodes video positions.
+ *
+ * For every row r < n_tok and head: the head's 128 elements are split into
+ * contiguous slices of widths d_t, d_h, d_w (in that order); inside a slice of
+ * width d, the pair (2i, 2i+1) is rotated by the angle pos_axis * theta^(-2i/d)
+ *   (x0, x1) <- (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+ * The rotation is evaluated in double precision and rounded once to bf16
+ * (nearest, ties to even). Text rows take no RoPE: do not pass them.
+ *
+ * x_in, x_out : bf16 [n_tok] rows with token stride `stride_tok` and head
+ *               stride `stride_head` (elements), shared by both; x_out == x_in
+ *               is allowed (in place); partial overlap is not.
+ * pos         : int32 [n_tok][3] = (t, h, w) integer latent-grid coordinates.
+ * Errors: EINVAL on null/misaligned pointers, n_tok < 0, n_heads < 1, bad
+ *   strides, theta <= 0; EUNSUPPORTED if head_dim != 128 or the widths are not
+ *   even and positive or do not sum to head_dim. n_tok == 0 is a no-op.
+ */
+int rope3d_apply(const void* x_in, void* x_out, int64_t n_tok, int32_t n_heads,
+                 int32_t head_dim, int64_t stride_tok, int64_t stride_head,
+                 const int32_t* pos, double theta, int32_t d_t, int32_t d_h,
+                 int32_t d_w, void* stream);
+
+/*
+ * kv_cache_append -- write the current segment's video K (after RoPE) and V
+ * into cache slots, quantising to INT8 when the cache is SEGC_INT8.
+ * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
+ * (cached keys and values are reused when generation advances) and section
+ * "Single-GPU Low-Memory Inference" (cached keys/values stored in INT8, BF16
+ * compute). The INT8 scheme is this library's: per (token, head)
+ *   scale = fp32(max|x| / 127)             (IEEE fp32 division)
+ *   code  = clamp(rint(fp32(x / scale)), -127, 127)   (ties to even)
+ * with scale = 0 and all codes 0 for an all-zero row; K and V separately.
+ * BF16 caches receive a plain copy.
+ *
+ * Frame f (0 <= f < n_frames) = input rows [f*G, (f+1)*G) goes to slot
+ * (first_slot + f) mod n_slots, so a ring of slots can wrap.
+ * k, v : bf16 [n_frames * G] rows, strides in elements (see conventions).
+ * Errors: EINVAL on null/misaligned pointers, a bad cache descriptor,
+ *   first_slot outside [0, n_slots), n_frames < 0 or > n_slots, bad strides.
+ */
+int kv_cache_append(const segc_cache* cache, int32_t first_slot, int32_t n_frames,
+                    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                    void* stream);
+
+/*
+ * window_select -- choose the cached frames the attention reads (host only).
+ * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
+ * (a bounded set of historical latent frames, default budget 18, excluding
+ * the current segment; full history when unbounded) and section "Single-GPU
+ * Low-Memory Inference" (up to 18 historical frames selected, older ones
+ * archived on CPU). This library's policy: the `budget` most recent valid
+ * frames by t, returned in ascending t.
+ *
+ * slot_t    : host int32 [n_slots]; slot_t[s] = latent-frame index held by
+ *             slot s, or -1 if the slot is empty.
+ * out_slots : host int32 [>= min(budget, n_slots)] receives slot indices.
+ * out_n     : host, receives the number written.
+ * Errors: EINVAL on null pointers, n_slots < 0, budget < 0, or two valid slots
+ *   with the same t.
+ */
+int window_select(const int32_t* slot_t, int32_t n_slots, int32_t budget,
+                  int32_t* out_slots, int32_t* out_n);
+
+/*
+ * segcausal_joint_attn -- segment-wise causal joint attention.
+ * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
+ * (joint text-video attention, the layer's KV cache supplies earlier
+ * segments, attention is causal across segments); "Hy-Nomas Explained ...",
+ * Step 2 "Segment-wise causal joint attention".
+ *
+ * Keys = the selected history rows (frames hist_slots[0..n_hist), G rows
+ * each) followed by the n_cur current rows. Current rows are n_seg packed
+ * segments, segment s spanning rows [seg_start[s], seg_start[s+1]) laid out
+ * [text (seg_text_len[s] rows) | video rows]. Query i of segment s sees key j
+ * iff j is a history row, or j is in segment s and is not a padded text row
+ * (text index >= seg_text_valid[s]), or j is a video row of a segment < s.
+ *   o_i   = sum_j softmax_j(sm_scale * q_i . k_j) v_j   over visible j
+ *   lse_i = natural log of sum_j exp(sm_scale * q_i . k_j)
+ * Computed with bf16 MFMA products and fp32 accumulation and softmax; INT8
+ * cache rows are dequantised to bf16 (bf16(code * scale)) as they are loaded.
+ */
+typedef struct segc_attn_args {
+  const void* q;   /* bf16 [n_cur] rows, current segment queries (video rows after RoPE) */
+  const void* k;   /* bf16 [n_cur] rows, current keys (video rows after RoPE) */
+  const void* v;   /* bf16 [n_cur] rows */
+  void*       o;   /* bf16 [n_cur] rows, output */
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  float*  lse;     /* optional fp32 [n_heads][n_cur]; NULL = not written */
+  int64_t n_cur;
+  int32_t n_heads;
+  int32_t head_dim;                /* must be 128 */
+  int32_t n_seg;                   /* 1 .. SEGC_MAX_SEG */
+  int32_t reserved;
+  const int32_t* seg_start;        /* host [n_seg + 1]: 0 = seg_start[0] < ... <= seg_start[n_seg] = n_cur */
+  const int32_t* seg_text_len;     /* host [n_seg] */
+  const int32_t* seg_text_valid;   /* host [n_seg], <= seg_text_len */
+  const segc_cache* cache;         /* NULL = no history */
+  const int32_t* hist_slots;       /* device int32 [n_hist], slot indices (e.g. from window_select) */
+  int32_t n_hist;                  /* number of history frames, 0 = none */
+  float   sm_scale;                /* > 0, e.g. 1/sqrt(128) */
+} segc_attn_args;
+
+/*
+ * Errors: EINVAL on null/misaligned pointers, n_cur < 0, bad strides, bad
+ *   segment tables (not starting at 0, not ascending, not ending at n_cur,
+ *   text_valid > text_len, text_len longer than its segment), a segment whose
+ *   queries would see no key, n_hist < 0 or > n_slots, n_hist > 0 without a
+ *   cache, a cache with n_heads different from the call's, sm_scale <= 0 or
+ *   not finite; EUNSUPPORTED if head_dim != 128 or n_seg outside
+ *   [1, SEGC_MAX_SEG]. n_cur == 0 is a no-op. Slot indices in hist_slots are
+ *   read on the device and must lie in [0, n_slots) (a precondition).
+ */
+int segcausal_joint_attn(const segc_attn_args* args, void* stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* segcausal_last_error(void);
+
+/* ABI version of this header, (major << 16) | minor. */
+int segcausal_abi_version(void);
+#define SEGC_ABI_VERSION ((1 << 16) | 0)
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGCAUSAL_H */

@@ -1,0 +1,216 @@
+"""Thin ctypes binding of libsegcausal.so (the C ABI in include/segcausal.h).
+
+Argument marshalling only: torch tensors supply device pointers, strides and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels. The names match the C entry points. If the library has not been
+built this module raises ImportError: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsegcausal.so")
+
+SEGC_OK, SEGC_EINVAL, SEGC_EUNSUPPORTED, SEGC_EHIP = 0, 1, 2, 3
+SEGC_BF16, SEGC_INT8 = 0, 1
+HEAD_DIM = 128
+MAX_SEG = 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libsegcausal.so is not built; run `python -m segment_causal_dit_amd.build` "
+        "(or __graft_entry__.build()) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class SegcCache(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("n_heads", _i32), ("head_dim", _i32),
+                ("tokens_per_frame", _i32), ("n_slots", _i32), ("reserved", _i32),
+                ("k", _vp), ("v", _vp), ("k_scale", _vp), ("v_scale", _vp)]
+
+
+class SegcAttnArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp),
+                ("q_stride_tok", _i64), ("q_stride_head", _i64),
+                ("k_stride_tok", _i64), ("k_stride_head", _i64),
+                ("v_stride_tok", _i64), ("v_stride_head", _i64),
+                ("o_stride_tok", _i64), ("o_stride_head", _i64),
+                ("lse", _vp), ("n_cur", _i64), ("n_heads", _i32), ("head_dim", _i32),
+                ("n_seg", _i32), ("reserved", _i32),
+                ("seg_start", _pi32), ("seg_text_len", _pi32), ("seg_text_valid", _pi32),
+                ("cache", ctypes.POINTER(SegcCache)), ("hist_slots", _vp),
+                ("n_hist", _i32), ("sm_scale", _f32)]
+
+
+_lib.rope3d_apply.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp, _f64, _i32, _i32, _i32, _vp]
+_lib.kv_cache_append.argtypes = [ctypes.POINTER(SegcCache), _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
+_lib.window_select.argtypes = [_pi32, _i32, _i32, _pi32, _pi32]
+_lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
+_lib.segcausal_last_error.restype = ctypes.c_char_p
+_lib.segcausal_abi_version.restype = ctypes.c_int
+for _f in ("rope3d_apply", "kv_cache_append", "window_select", "segcausal_joint_attn"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+EXPORTS = ("rope3d_apply", "kv_cache_append", "window_select", "segcausal_joint_attn",
+           "segcausal_last_error", "segcausal_abi_version")
+
+
+class SegcError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("segcausal status %d: %s" % (code, msg))
+        self.code = code
+
+
+def _check(rc):
+    if rc != SEGC_OK:
+        raise SegcError(rc, _lib.segcausal_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return _vp(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return _vp(stream.cuda_stream)
+    return _vp(stream)
+
+
+def _rows(t, name):
+    """(pointer, token stride, head stride) of a [rows, heads, 128] bf16 tensor."""
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or t.shape[2] != HEAD_DIM or t.stride(2) != 1:
+        raise ValueError("%s must be bf16 [rows, heads, 128] with contiguous last dim" % name)
+    return t.data_ptr(), t.stride(0), t.stride(1)
+
+
+def abi_version():
+    return _lib.segcausal_abi_version()
+
+
+def rope3d_apply(x_in, pos, x_out=None, theta=256.0, dims=(16, 56, 56), stream=None):
+    """Rotate video rows in place (x_out None) or into x_out (same layout)."""
+    if x_out is None:
+        x_out = x_in
+    pi, st, sh = _rows(x_in, "x_in")
+    po, st2, sh2 = _rows(x_out, "x_out")
+    if (st, sh) != (st2, sh2) or x_out.shape != x_in.shape:
+        raise ValueError("x_in and x_out must share shape and strides")
+    if pos.dtype != torch.int32 or not pos.is_contiguous() or tuple(pos.shape) != (x_in.shape[0], 3):
+        raise ValueError("pos must be contiguous int32 [rows, 3]")
+    _check(_lib.rope3d_apply(pi, po, x_in.shape[0], x_in.shape[1], HEAD_DIM, st, sh,
+                             pos.data_ptr(), float(theta), dims[0], dims[1], dims[2],
+                             _stream(stream)))
+    return x_out
+
+
+class KVCache:
+    """Device memory of one layer's cache plus its C descriptor.
+
+    k, v   : [n_slots, n_heads, G, 128] int8 or bf16
+    k_scale, v_scale : [n_slots, n_heads, G] fp32 (INT8 only)
+    slot_t : host numpy int32 [n_slots], latent-frame index held by each slot
+    """
+
+    def __init__(self, n_slots, n_heads, tokens_per_frame, dtype="int8", device="cuda"):
+        shape = (n_slots, n_heads, tokens_per_frame, HEAD_DIM)
+        self.int8 = dtype == "int8"
+        tdt = torch.int8 if self.int8 else torch.bfloat16
+        self.k = torch.zeros(shape, dtype=tdt, device=device)
+        self.v = torch.zeros(shape, dtype=tdt, device=device)
+        if self.int8:
+            self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+            self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+        else:
+            self.k_scale = self.v_scale = None
+        self.slot_t = np.full(n_slots, -1, dtype=np.int32)
+        self.desc = SegcCache(SEGC_INT8 if self.int8 else SEGC_BF16, n_heads, HEAD_DIM,
+                              tokens_per_frame, n_slots, 0, self.k.data_ptr(), self.v.data_ptr(),
+                              self.k_scale.data_ptr() if self.int8 else None,
+                              self.v_scale.data_ptr() if self.int8 else None)
+
+    @property
+    def n_slots(self):
+        return self.desc.n_slots
+
+    @property
+    def tokens_per_frame(self):
+        return self.desc.tokens_per_frame
+
+
+def kv_cache_append(cache, first_slot, k, v, t_first=None, stream=None):
+    """Append n_frames * G rows of post-RoPE K and of V into slots
+    first_slot, first_slot + 1, ... (mod n_slots). If t_first is given the
+    host slot table records frames t_first, t_first + 1, ..."""
+    pk, kst, ksh = _rows(k, "k")
+    pv, vst, vsh = _rows(v, "v")
+    g = cache.tokens_per_frame
+    if k.shape[0] != v.shape[0] or k.shape[0] % g:
+        raise ValueError("k and v must hold the same whole number of frames")
+    n_frames = k.shape[0] // g
+    _check(_lib.kv_cache_append(ctypes.byref(cache.desc), first_slot, n_frames,
+                                pk, kst, ksh, pv, vst, vsh, _stream(stream)))
+    if t_first is not None:
+        for f in range(n_frames):
+            cache.slot_t[(first_slot + f) % cache.n_slots] = t_first + f
+    return n_frames
+
+
+def window_select(slot_t, budget):
+    """Host-side window: slot indices of the `budget` most recent frames."""
+    st = np.ascontiguousarray(slot_t, dtype=np.int32)
+    out = np.zeros(max(1, min(budget, len(st))) if budget >= 0 else 1, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(_lib.window_select(st.ctypes.data_as(_pi32), len(st), int(budget),
+                              out.ctypes.data_as(_pi32), ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def segcausal_joint_attn(q, k, v, segments, sm_scale, cache=None, hist_slots=None, out=None,
+                         lse=None, stream=None):
+    """Segment-wise causal joint attention.
+
+    q, k, v    : bf16 [n_cur, H, 128] (video rows already rotated)
+    segments   : list of (start, text_len, text_valid)
+    cache      : KVCache or None; hist_slots: device int32 tensor [n_hist]
+    out        : optional bf16 [n_cur, H, 128]; lse: optional fp32 [H, n_cur]
+    """
+    pq, qst, qsh = _rows(q, "q")
+    pk, kst, ksh = _rows(k, "k")
+    pv, vst, vsh = _rows(v, "v")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    po, ost, osh = _rows(out, "out")
+    n_cur, nh = q.shape[0], q.shape[1]
+    starts = [int(s[0]) for s in segments] + [n_cur]
+    seg_start = (ctypes.c_int32 * len(starts))(*starts)
+    tl = (ctypes.c_int32 * max(1, len(segments)))(*[int(s[1]) for s in segments])
+    tv = (ctypes.c_int32 * max(1, len(segments)))(*[int(s[2]) for s in segments])
+    n_hist = 0
+    hs_ptr = None
+    cache_ptr = None
+    if hist_slots is not None and hist_slots.numel() > 0:
+        if hist_slots.dtype != torch.int32 or not hist_slots.is_contiguous():
+            raise ValueError("hist_slots must be a contiguous int32 device tensor")
+        n_hist = hist_slots.numel()
+        hs_ptr = hist_slots.data_ptr()
+    if cache is not None:
+        cache_ptr = ctypes.pointer(cache.desc)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (nh, n_cur)
+                            or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous fp32 [H, n_cur]")
+    args = SegcAttnArgs(pq, pk, pv, po, qst, qsh, kst, ksh, vst, vsh, ost, osh,
+                        lse.data_ptr() if lse is not None else None, n_cur, nh, HEAD_DIM,
+                        len(segments), 0, seg_start, tl, tv, cache_ptr, hs_ptr, n_hist,
+                        float(sm_scale))
+    _check(_lib.segcausal_joint_attn(ctypes.byref(args), _stream(stream)))
+    return out
+
+
+def raw_library():
+    """The loaded ctypes library (for ABI-level tests)."""
+    return _lib

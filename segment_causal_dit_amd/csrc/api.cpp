@@ -1,0 +1,264 @@
+// Host side of libsegcausal.so: argument checks, error reporting, window
+// selection and kernel launches. Every check runs before anything is
+// launched, so a non-zero status means nothing was written.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SEGC_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SEGC_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool strides_ok(int64_t st, int64_t sh) {
+  return st >= 0 && sh >= 0 && st % 8 == 0 && sh % 8 == 0;
+}
+
+int check_cache(const segc_cache* c) {
+  if (!c) return fail(SEGC_EINVAL, "cache descriptor is NULL");
+  if (c->dtype != SEGC_BF16 && c->dtype != SEGC_INT8)
+    return fail(SEGC_EINVAL, "cache dtype %d is neither SEGC_BF16 nor SEGC_INT8", c->dtype);
+  if (c->head_dim != SEGC_HEAD_DIM)
+    return fail(SEGC_EUNSUPPORTED, "cache head_dim %d != 128", c->head_dim);
+  if (c->n_heads < 1 || c->tokens_per_frame < 1 || c->n_slots < 1)
+    return fail(SEGC_EINVAL, "cache n_heads, tokens_per_frame and n_slots must be >= 1");
+  if ((int64_t)c->n_slots * c->n_heads * c->tokens_per_frame > ((int64_t)1 << 40))
+    return fail(SEGC_EINVAL, "cache is too large");
+  if (!c->k || !c->v) return fail(SEGC_EINVAL, "cache k/v pointer is NULL");
+  if (!aligned16(c->k) || !aligned16(c->v))
+    return fail(SEGC_EINVAL, "cache k/v pointers must be 16-byte aligned");
+  if (c->dtype == SEGC_INT8) {
+    if (!c->k_scale || !c->v_scale) return fail(SEGC_EINVAL, "INT8 cache needs k_scale and v_scale");
+    if (((uintptr_t)c->k_scale & 3u) || ((uintptr_t)c->v_scale & 3u))
+      return fail(SEGC_EINVAL, "cache scales must be 4-byte aligned");
+  }
+  return SEGC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* segcausal_last_error(void) { return g_err; }
+
+int segcausal_abi_version(void) { return SEGC_ABI_VERSION; }
+
+int rope3d_apply(const void* x_in, void* x_out, int64_t n_tok, int32_t n_heads, int32_t head_dim,
+                 int64_t stride_tok, int64_t stride_head, const int32_t* pos, double theta,
+                 int32_t d_t, int32_t d_h, int32_t d_w, void* stream) {
+  if (head_dim != SEGC_HEAD_DIM) return fail(SEGC_EUNSUPPORTED, "head_dim %d != 128", head_dim);
+  if (d_t <= 0 || d_h <= 0 || d_w <= 0 || (d_t | d_h | d_w) & 1 || d_t + d_h + d_w != head_dim)
+    return fail(SEGC_EUNSUPPORTED, "RoPE widths (%d, %d, %d) must be even, positive, sum to 128",
+                d_t, d_h, d_w);
+  if (n_tok < 0 || n_tok > ((int64_t)1 << 32)) return fail(SEGC_EINVAL, "n_tok out of range");
+  if (n_heads < 1 || n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  if (!(theta > 0.0) || !std::isfinite(theta)) return fail(SEGC_EINVAL, "theta must be > 0");
+  if (!strides_ok(stride_tok, stride_head))
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+  if (n_tok == 0) return ok();
+  if (!x_in || !x_out || !pos) return fail(SEGC_EINVAL, "NULL pointer");
+  if (!aligned16(x_in) || !aligned16(x_out))
+    return fail(SEGC_EINVAL, "x_in/x_out must be 16-byte aligned");
+  if (((uintptr_t)pos & 3u)) return fail(SEGC_EINVAL, "pos must be 4-byte aligned");
+  segc::RopeParams p;
+  p.x_in = (const uint16_t*)x_in;
+  p.x_out = (uint16_t*)x_out;
+  p.pos = pos;
+  p.n_tok = n_tok;
+  p.stride_tok = stride_tok;
+  p.stride_head = stride_head;
+  p.n_heads = n_heads;
+  p.dims[0] = d_t;
+  p.dims[1] = d_h;
+  p.dims[2] = d_w;
+  const int widths[3] = {d_t, d_h, d_w};
+  int pr = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int i = 0; i < widths[a] / 2; ++i)
+      p.inv_freq[pr++] = std::pow(theta, -2.0 * (double)i / (double)widths[a]);
+  return hip_status(segc::launch_rope(p, (hipStream_t)stream), "rope3d_apply launch");
+}
+
+int kv_cache_append(const segc_cache* cache, int32_t first_slot, int32_t n_frames, const void* k,
+                    int64_t k_stride_tok, int64_t k_stride_head, const void* v,
+                    int64_t v_stride_tok, int64_t v_stride_head, void* stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (first_slot < 0 || first_slot >= cache->n_slots)
+    return fail(SEGC_EINVAL, "first_slot %d outside [0, %d)", first_slot, cache->n_slots);
+  if (n_frames < 0 || n_frames > cache->n_slots)
+    return fail(SEGC_EINVAL, "n_frames %d outside [0, n_slots=%d]", n_frames, cache->n_slots);
+  if (!strides_ok(k_stride_tok, k_stride_head) || !strides_ok(v_stride_tok, v_stride_head))
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+  const int64_t n_tok = (int64_t)n_frames * cache->tokens_per_frame;
+  if (n_tok > (int64_t)1 << 30) return fail(SEGC_EINVAL, "append too large");
+  if (n_frames == 0) return ok();
+  if (!k || !v) return fail(SEGC_EINVAL, "NULL k or v");
+  if (!aligned16(k) || !aligned16(v)) return fail(SEGC_EINVAL, "k/v must be 16-byte aligned");
+  segc::AppendParams p;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.k_st = k_stride_tok;
+  p.k_sh = k_stride_head;
+  p.v_st = v_stride_tok;
+  p.v_sh = v_stride_head;
+  p.ck = cache->k;
+  p.cv = cache->v;
+  p.cks = cache->k_scale;
+  p.cvs = cache->v_scale;
+  p.n_tok = (int32_t)n_tok;
+  p.G = cache->tokens_per_frame;
+  p.n_heads = cache->n_heads;
+  p.n_slots = cache->n_slots;
+  p.first_slot = first_slot;
+  p.int8 = cache->dtype == SEGC_INT8;
+  return hip_status(segc::launch_append(p, (hipStream_t)stream), "kv_cache_append launch");
+}
+
+int window_select(const int32_t* slot_t, int32_t n_slots, int32_t budget, int32_t* out_slots,
+                  int32_t* out_n) {
+  if (n_slots < 0) return fail(SEGC_EINVAL, "n_slots < 0");
+  if (budget < 0) return fail(SEGC_EINVAL, "budget < 0");
+  if (!out_n || (n_slots > 0 && !slot_t)) return fail(SEGC_EINVAL, "NULL pointer");
+  std::vector<std::pair<int32_t, int32_t>> valid;   // (t, slot)
+  valid.reserve(n_slots);
+  for (int32_t s = 0; s < n_slots; ++s)
+    if (slot_t[s] >= 0) valid.emplace_back(slot_t[s], s);
+  std::sort(valid.begin(), valid.end());
+  for (size_t i = 1; i < valid.size(); ++i)
+    if (valid[i].first == valid[i - 1].first)
+      return fail(SEGC_EINVAL, "slots %d and %d both hold t = %d", valid[i - 1].second,
+                  valid[i].second, valid[i].first);
+  const size_t keep = std::min<size_t>((size_t)budget, valid.size());
+  if (keep > 0 && !out_slots) return fail(SEGC_EINVAL, "NULL out_slots");
+  const size_t first = valid.size() - keep;
+  for (size_t i = 0; i < keep; ++i) out_slots[i] = valid[first + i].second;
+  *out_n = (int32_t)keep;
+  return ok();
+}
+
+int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
+  if (!a) return fail(SEGC_EINVAL, "args is NULL");
+  if (a->head_dim != SEGC_HEAD_DIM) return fail(SEGC_EUNSUPPORTED, "head_dim %d != 128", a->head_dim);
+  if (a->n_seg < 1 || a->n_seg > SEGC_MAX_SEG)
+    return fail(SEGC_EUNSUPPORTED, "n_seg %d outside [1, %d]", a->n_seg, SEGC_MAX_SEG);
+  if (a->n_cur < 0 || a->n_cur > (int64_t)1 << 30) return fail(SEGC_EINVAL, "n_cur out of range");
+  if (a->n_heads < 1 || a->n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
+    return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
+  if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->k_stride_tok, a->k_stride_head) ||
+      !strides_ok(a->v_stride_tok, a->v_stride_head) || !strides_ok(a->o_stride_tok, a->o_stride_head))
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+  if (!a->seg_start || !a->seg_text_len || !a->seg_text_valid)
+    return fail(SEGC_EINVAL, "NULL segment table");
+  if (a->seg_start[0] != 0) return fail(SEGC_EINVAL, "seg_start[0] must be 0");
+  if (a->seg_start[a->n_seg] != a->n_cur)
+    return fail(SEGC_EINVAL, "seg_start[n_seg] = %d != n_cur", a->seg_start[a->n_seg]);
+  for (int s = 0; s < a->n_seg; ++s) {
+    const int len = a->seg_start[s + 1] - a->seg_start[s];
+    if (len < 0) return fail(SEGC_EINVAL, "seg_start not ascending at %d", s);
+    if (a->seg_text_len[s] < 0 || a->seg_text_len[s] > len)
+      return fail(SEGC_EINVAL, "segment %d: text_len %d outside [0, %d]", s, a->seg_text_len[s], len);
+    if (a->seg_text_valid[s] < 0 || a->seg_text_valid[s] > a->seg_text_len[s])
+      return fail(SEGC_EINVAL, "segment %d: text_valid %d > text_len %d", s, a->seg_text_valid[s],
+                  a->seg_text_len[s]);
+  }
+  if (a->n_hist < 0) return fail(SEGC_EINVAL, "n_hist < 0");
+  int64_t n_hist_rows = 0;
+  int hist_int8 = 0;
+  if (a->n_hist > 0) {
+    if (!a->cache) return fail(SEGC_EINVAL, "n_hist > 0 without a cache");
+    int rc = check_cache(a->cache);
+    if (rc) return rc;
+    if (a->cache->n_heads != a->n_heads)
+      return fail(SEGC_EINVAL, "cache has %d heads, call has %d", a->cache->n_heads, a->n_heads);
+    if (a->n_hist > a->cache->n_slots)
+      return fail(SEGC_EINVAL, "n_hist %d > n_slots %d", a->n_hist, a->cache->n_slots);
+    if (!a->hist_slots) return fail(SEGC_EINVAL, "NULL hist_slots");
+    n_hist_rows = (int64_t)a->n_hist * a->cache->tokens_per_frame;
+    if (n_hist_rows > (int64_t)1 << 30) return fail(SEGC_EINVAL, "history too long");
+    hist_int8 = a->cache->dtype == SEGC_INT8;
+  }
+  // every query must see at least one key
+  int64_t earlier_video = 0;
+  for (int s = 0; s < a->n_seg; ++s) {
+    const int len = a->seg_start[s + 1] - a->seg_start[s];
+    const int64_t visible = n_hist_rows + earlier_video + a->seg_text_valid[s] + (len - a->seg_text_len[s]);
+    if (len > 0 && visible == 0) return fail(SEGC_EINVAL, "segment %d has no visible key", s);
+    earlier_video += len - a->seg_text_len[s];
+  }
+  if (a->n_cur == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->o) return fail(SEGC_EINVAL, "NULL q/k/v/o");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(SEGC_EINVAL, "q/k/v/o must be 16-byte aligned");
+  if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(SEGC_EINVAL, "lse must be 4-byte aligned");
+
+  segc::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t*)a->q;
+  p.k = (const uint16_t*)a->k;
+  p.v = (const uint16_t*)a->v;
+  p.o = (uint16_t*)a->o;
+  p.lse = a->lse;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.k_st = a->k_stride_tok;
+  p.k_sh = a->k_stride_head;
+  p.v_st = a->v_stride_tok;
+  p.v_sh = a->v_stride_head;
+  p.o_st = a->o_stride_tok;
+  p.o_sh = a->o_stride_head;
+  if (a->n_hist > 0) {
+    p.hk = a->cache->k;
+    p.hv = a->cache->v;
+    p.hks = a->cache->k_scale;
+    p.hvs = a->cache->v_scale;
+    p.hist_slots = a->hist_slots;
+    p.G = a->cache->tokens_per_frame;
+    p.n_hist_rows = (int32_t)n_hist_rows;
+    p.hist_tiles = (int32_t)((n_hist_rows + 63) / 64);
+    p.hist_int8 = hist_int8;
+  } else {
+    p.G = 1;
+  }
+  p.n_cur = (int32_t)a->n_cur;
+  p.n_heads = a->n_heads;
+  p.n_seg = a->n_seg;
+  bool needs_mask = a->n_seg > 1;
+  for (int s = 0; s <= a->n_seg; ++s) p.seg_start[s] = a->seg_start[s];
+  for (int s = 0; s < a->n_seg; ++s) {
+    p.seg_text_len[s] = a->seg_text_len[s];
+    p.seg_text_valid[s] = a->seg_text_valid[s];
+    needs_mask = needs_mask || a->seg_text_valid[s] < a->seg_text_len[s];
+  }
+  p.needs_mask = needs_mask;
+  p.sm_scale = a->sm_scale;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  return hip_status(segc::launch_attn(p, (hipStream_t)stream), "segcausal_joint_attn launch");
+}
+
+}  // extern "C"

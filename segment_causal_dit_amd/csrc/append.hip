@@ -1,0 +1,108 @@
+// Append the current segment's video K (after RoPE) and V to cache slots,
+// quantising to INT8 for an INT8 cache.
+//
+// Source: "Hy-Nomas: Towards Free-Form Interactive World Generation", section
+// "Segment-Autoregressive Diffusion Transformer" (cached keys and values are
+// reused when generation advances) and section "Single-GPU Low-Memory
+// Inference" (keys and values cached in INT8, attention kept in BF16).
+// Quantiser (this library's scheme, per token and head, K and V separately):
+//   scale = fp32(max|x| / 127)                       IEEE fp32 division
+//   code  = clamp(rint(fp32(x / scale)), -127, 127)  ties to even
+// with scale 0 and all-zero codes for an all-zero row.
+//
+// x / scale is first estimated as x * fp32(1/scale). That estimate is within
+// 2^-16 of the exact quotient and the IEEE quotient within 2^-18, so unless
+// the estimate lies within 2^-15 of a half-integer both round to the same
+// integer; otherwise the IEEE division is done. Codes are bit-exact.
+//
+// Layout: a workgroup of 256 lanes handles 16 consecutive tokens of one head;
+// 16 lanes per (token, head), 8 elements each. HBM-bound: 776 B per
+// (token, head) moved for INT8 (512 read, 256 codes + 8 scale bytes written),
+// 1024 B for a BF16 cache.
+#include "internal.h"
+
+namespace segc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokPerBlock = 16;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline int quant_one(float x, float rcp, float scale) {
+  float q = x * rcp;
+  const float fr = q - floorf(q);
+  if (fabsf(fr - 0.5f) <= 0x1p-15f) q = x / scale;   // IEEE quotient decides
+  const int c = (int)rintf(q);
+  return c < -127 ? -127 : (c > 127 ? 127 : c);
+}
+
+// Quantise 8 bf16 values held by this lane (one of 16 lanes of a row);
+// returns the 8 codes packed little-endian and the row's scale.
+__device__ inline u32x2 quant_row8(const u32x4 in, float* scale_out) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(in[i]);
+    x[2 * i + 1] = bf16_hi(in[i]);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
+  const float scale = a / 127.0f;                    // IEEE fp32 division
+  *scale_out = scale;
+  u32x2 out = {0u, 0u};
+  if (scale != 0.0f) {
+    const float rcp = 1.0f / scale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = (uint32_t)quant_one(x[i], rcp, scale) & 0xFFu;
+      out[i >> 2] |= b << (8 * (i & 3));
+    }
+  }
+  return out;
+}
+
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {
+  const int tid = threadIdx.x;
+  const int head = blockIdx.y;
+  const int r = blockIdx.x * kTokPerBlock + (tid >> 4);   // input token
+  const int li = tid & 15;                                  // 8-element chunk
+  if (r >= p.n_tok) return;        // whole 16-lane groups exit together
+  const int f = r / p.G;
+  const int g = r - f * p.G;
+  const int slot = (p.first_slot + f) % p.n_slots;
+  const int64_t row = ((int64_t)slot * p.n_heads + head) * p.G + g;   // cache row
+  const u32x4 kin = *(const u32x4*)(p.k + r * p.k_st + head * p.k_sh + li * 8);
+  const u32x4 vin = *(const u32x4*)(p.v + r * p.v_st + head * p.v_sh + li * 8);
+  if (p.int8) {
+    float ks, vs;
+    const u32x2 kc = quant_row8(kin, &ks);
+    const u32x2 vc = quant_row8(vin, &vs);
+    *(u32x2*)((int8_t*)p.ck + row * 128 + li * 8) = kc;
+    *(u32x2*)((int8_t*)p.cv + row * 128 + li * 8) = vc;
+    if (li == 0) {
+      p.cks[row] = ks;
+      p.cvs[row] = vs;
+    }
+  } else {
+    *(u32x4*)((uint16_t*)p.ck + row * 128 + li * 8) = kin;
+    *(u32x4*)((uint16_t*)p.cv + row * 128 + li * 8) = vin;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  const unsigned bx = (unsigned)((p.n_tok + kTokPerBlock - 1) / kTokPerBlock);
+  hipLaunchKernelGGL(append_kernel, dim3(bx, (unsigned)p.n_heads), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace segc

@@ -1,0 +1,76 @@
+// Internal declarations shared by the library's HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "segcausal.h"
+
+namespace segc {
+
+// ------------------------------------------------------------- RoPE ----
+struct RopeParams {
+  const uint16_t* x_in;
+  uint16_t* x_out;
+  const int32_t* pos;
+  int64_t n_tok;
+  int64_t stride_tok, stride_head;   // elements
+  int32_t n_heads;
+  int32_t dims[3];                   // t, h, w slice widths
+  double inv_freq[64];               // theta^(-2i/d) per pair, t pairs then h then w
+};
+hipError_t launch_rope(const RopeParams& p, hipStream_t s);
+
+// ----------------------------------------------------------- append ----
+struct AppendParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_st, k_sh, v_st, v_sh;    // elements
+  void* ck;                          // cache K (int8 codes or bf16)
+  void* cv;
+  float* cks;                        // cache scales (INT8)
+  float* cvs;
+  int32_t n_tok;                     // n_frames * G
+  int32_t G;
+  int32_t n_heads;
+  int32_t n_slots;
+  int32_t first_slot;
+  int32_t int8;
+};
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
+// -------------------------------------------------------- attention ----
+constexpr int kMaxSeg = SEGC_MAX_SEG;
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;   // elements
+  // history (cache) view
+  const void* hk;
+  const void* hv;
+  const float* hks;
+  const float* hvs;
+  const int32_t* hist_slots;
+  int32_t n_hist_rows;       // n_hist * G
+  int32_t hist_tiles;        // ceil(n_hist_rows / 64)
+  int32_t G;
+  int32_t hist_int8;
+  // current segment(s)
+  int32_t n_cur;
+  int32_t n_heads;
+  int32_t n_qtiles;
+  int32_t n_seg;
+  int32_t needs_mask;        // segment structure beyond one unpadded segment
+  float sm_scale;
+  float scale_log2;          // sm_scale * log2(e)
+  int32_t seg_start[kMaxSeg + 1];
+  int32_t seg_text_len[kMaxSeg];
+  int32_t seg_text_valid[kMaxSeg];
+};
+hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+
+}  // namespace segc

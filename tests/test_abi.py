@@ -1,0 +1,167 @@
+"""C-ABI tests that need no GPU: exports, host-only window selection, and
+every argument check (each fails on the host before anything is launched)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "segcausal.h")
+
+sc = pytest.importorskip("segment_causal_dit_amd._lib",
+                         reason="libsegcausal.so not built (run __graft_entry__.build())")
+lib = sc.raw_library()
+FAKE = 0x10000000          # a 16-byte aligned stand-in pointer: never dereferenced
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(sc.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.segcausal_abi_version() == (1 << 16)
+
+
+def test_window_select_matches_oracle():
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        n = int(rng.integers(0, 40))
+        ts = rng.permutation(500)[:n].astype(np.int32)
+        ts[rng.random(n) < 0.25] = -1
+        for b in (0, 1, 5, 18, 64):
+            assert list(sc.window_select(ts, b)) == list(oracle.window_select(ts, b))
+
+
+def test_window_select_errors():
+    with pytest.raises(sc.SegcError) as e:
+        sc.window_select(np.array([4, 1, 4], np.int32), 2)
+    assert e.value.code == sc.SEGC_EINVAL and "t = 4" in str(e.value)
+    with pytest.raises(sc.SegcError):
+        sc.window_select(np.array([1], np.int32), -1)
+    assert list(sc.window_select(np.array([], np.int32), 3)) == []
+
+
+# ------------------------------------------------------------- rope ----
+
+def _rope(**kw):
+    a = dict(x_in=FAKE, x_out=FAKE, n_tok=10, n_heads=16, head_dim=128, st=2048, sh=128,
+             pos=FAKE, theta=256.0, dt=16, dh=56, dw=56)
+    a.update(kw)
+    return lib.rope3d_apply(a["x_in"], a["x_out"], a["n_tok"], a["n_heads"], a["head_dim"],
+                            a["st"], a["sh"], a["pos"], a["theta"], a["dt"], a["dh"], a["dw"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), 2), (dict(dt=15, dh=57), 2), (dict(dt=16, dh=56, dw=58), 2),
+    (dict(dt=0, dh=72), 2), (dict(n_tok=-1), 1), (dict(n_heads=0), 1), (dict(theta=0.0), 1),
+    (dict(theta=float("nan")), 1), (dict(st=2047), 1), (dict(sh=-8), 1), (dict(x_in=None), 1),
+    (dict(pos=None), 1), (dict(x_out=FAKE + 8), 1), (dict(pos=FAKE + 2), 1),
+])
+def test_rope_rejects(kw, code):
+    assert _rope(**kw) == code
+    assert lib.segcausal_last_error().decode()
+
+
+def test_rope_zero_tokens_is_noop():
+    assert _rope(n_tok=0, x_in=None, x_out=None, pos=None) == 0
+
+
+# ----------------------------------------------------------- append ----
+
+def _cache(**kw):
+    c = sc.SegcCache(sc.SEGC_INT8, 16, 128, 880, 8, 0, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _append(cache=None, first=0, n=2, k=FAKE, v=FAKE, kst=2048, ksh=128):
+    c = cache if cache is not None else _cache()
+    return lib.kv_cache_append(ctypes.byref(c), first, n, k, kst, ksh, v, 2048, 128, None)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(cache=_cache(dtype=5)), 1), (dict(cache=_cache(head_dim=64)), 2),
+    (dict(cache=_cache(n_slots=0)), 1), (dict(cache=_cache(k=None)), 1),
+    (dict(cache=_cache(k_scale=None)), 1), (dict(cache=_cache(v=FAKE + 4)), 1),
+    (dict(first=8), 1), (dict(first=-1), 1), (dict(n=9), 1), (dict(n=-1), 1),
+    (dict(k=None), 1), (dict(kst=100), 1), (dict(k=FAKE + 2), 1),
+])
+def test_append_rejects(args, code):
+    assert _append(**args) == code
+
+
+def test_append_null_cache_and_noop():
+    assert lib.kv_cache_append(None, 0, 1, FAKE, 2048, 128, FAKE, 2048, 128, None) == 1
+    assert _append(n=0, k=None, v=None) == 0
+    # a BF16 cache needs no scales
+    assert _append(cache=_cache(dtype=sc.SEGC_BF16, k_scale=None, v_scale=None), n=0) == 0
+
+
+# -------------------------------------------------------- attention ----
+
+def _attn(segs=((0, 16, 16),), n_cur=None, **kw):
+    n_cur = n_cur if n_cur is not None else 64
+    starts = [s[0] for s in segs] + [n_cur]
+    ss = (ctypes.c_int32 * len(starts))(*starts)
+    tl = (ctypes.c_int32 * len(segs))(*[s[1] for s in segs])
+    tv = (ctypes.c_int32 * len(segs))(*[s[2] for s in segs])
+    a = sc.SegcAttnArgs(FAKE, FAKE, FAKE, FAKE, 256, 128, 256, 128, 256, 128, 256, 128,
+                        None, n_cur, 2, 128, len(segs), 0, ss, tl, tv, None, None, 0, 0.088)
+    cache = kw.pop("cache", None)
+    if cache is not None:
+        a.cache = ctypes.pointer(cache)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return lib.segcausal_joint_attn(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), 2), (dict(n_seg=0), 2), (dict(n_seg=17), 2),
+    (dict(n_cur=-1), 1), (dict(n_heads=0), 1), (dict(sm_scale=0.0), 1),
+    (dict(sm_scale=float("inf")), 1), (dict(q_stride_tok=100), 1), (dict(o_stride_head=-8), 1),
+    (dict(q=None), 1), (dict(o=FAKE + 8), 1), (dict(lse=FAKE + 2), 1),
+    (dict(n_hist=-1), 1), (dict(n_hist=2), 1),                       # history without a cache
+    (dict(n_hist=2, cache=_cache(n_heads=2)), 1),                   # hist_slots missing
+    (dict(n_hist=9, cache=_cache(n_heads=2), hist_slots=FAKE), 1),  # more frames than slots
+    (dict(n_hist=2, cache=_cache(), hist_slots=FAKE), 1),           # head count mismatch
+    (dict(n_hist=2, cache=_cache(n_heads=2, head_dim=64), hist_slots=FAKE), 2),
+])
+def test_attn_rejects(kw, code):
+    assert _attn(**kw) == code
+    assert lib.segcausal_last_error().decode()
+
+
+@pytest.mark.parametrize("segs,n_cur", [
+    (((1, 0, 0),), 64),                   # does not start at 0
+    (((0, 16, 16),), 70),                 # n_cur disagrees with seg_start[n_seg] below
+    (((0, 16, 17),), 64),                 # text_valid > text_len
+    (((0, 65, 10),), 64),                 # text longer than the segment
+    (((0, 4, 4), (50, 2, 2), (40, 0, 0)), 64),   # not ascending
+    (((0, 8, 0),), 8),                    # only padded text: no visible key
+])
+def test_attn_rejects_bad_segments(segs, n_cur):
+    if n_cur == 70:
+        starts = (ctypes.c_int32 * 2)(0, 64)
+        a = sc.SegcAttnArgs(FAKE, FAKE, FAKE, FAKE, 256, 128, 256, 128, 256, 128, 256, 128,
+                            None, 70, 2, 128, 1, 0, starts, (ctypes.c_int32 * 1)(16),
+                            (ctypes.c_int32 * 1)(16), None, None, 0, 0.088)
+        assert lib.segcausal_joint_attn(ctypes.byref(a), None) == 1
+        return
+    assert _attn(segs=segs, n_cur=n_cur) == 1
+
+
+def test_attn_noop_and_null_args():
+    assert lib.segcausal_joint_attn(None, None) == 1
+    assert _attn(segs=((0, 0, 0),), n_cur=0, q=None, k=None, v=None, o=None) == 0

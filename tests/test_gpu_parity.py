@@ -1,0 +1,304 @@
+"""GPU parity: the HIP library (called through the C ABI) against the fp64
+CPU oracle on the same seeded inputs.
+
+Bars: RoPE outputs, INT8 codes and scales and BF16 cache copies bit-exact;
+attention outputs max |err| <= 1e-2 and mean |err| <= 1e-3 (unit-variance
+inputs); lse max |err| <= 5e-3 (a derived bound: bf16 rounding of P and of
+dequantised keys perturbs the logits by far less than this at these sizes).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import HEAD_DIM
+from chain import attn_errors, bits, gpu_chain, oracle_cache, oracle_chain, oracle_inputs, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+sc = pytest.importorskip("segment_causal_dit_amd._lib")
+
+MAX_ERR, MEAN_ERR, LSE_ERR = 1e-2, 1e-3, 5e-3
+SMALL = ["c0", "c0_int8", "c0_win3", "c0_pad", "c0_packed3",
+         "mid_int8", "mid_bf16", "mid_packed", "mid_nocache"]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _bf(x_bits, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+# ------------------------------------------------------------------ RoPE ----
+
+@pytest.mark.parametrize("name", ["c0", "mid_packed", "c1"])
+def test_rope_bit_exact(name):
+    _say("rope", name)
+    inp = workloads.make_inputs(name)
+    x = _bf(inp.k[inp.video_rows])
+    sc.rope3d_apply(x, torch.from_numpy(inp.pos).cuda())
+    want = oracle.f64_to_bf16_bits(oracle.rope3d_bf16(inp.k[inp.video_rows], inp.pos))
+    got = bits(x)
+    assert np.array_equal(got, want), "%d of %d differ" % ((got != want).sum(), got.size)
+
+
+def test_rope_large_positions_strided_out_of_place():
+    rng = np.random.default_rng(21)
+    n, h = 3000, 4
+    qkv = workloads.normal_bf16(7, (n, 3, h, HEAD_DIM))
+    pos = np.stack([rng.integers(0, 20000, n), rng.integers(0, 300, n),
+                    rng.integers(0, 300, n)], axis=1).astype(np.int32)
+    t = _bf(qkv)
+    src = t[:, 1]                                  # token stride 3*h*128
+    dst_buf = torch.zeros_like(t)
+    dst = dst_buf[:, 1]
+    sc.rope3d_apply(src, torch.from_numpy(pos).cuda(), x_out=dst)
+    want = oracle.f64_to_bf16_bits(oracle.rope3d_bf16(qkv[:, 1], pos))
+    assert np.array_equal(bits(dst), want)
+    assert not bits(dst_buf[:, 0]).any() and not bits(dst_buf[:, 2]).any()
+    assert np.array_equal(bits(t), qkv)            # input untouched
+
+
+def test_rope_other_split_and_theta():
+    inp = workloads.make_inputs("mid_bf16")
+    x = _bf(inp.q[inp.video_rows])
+    sc.rope3d_apply(x, torch.from_numpy(inp.pos).cuda(), theta=10000.0, dims=(32, 48, 48))
+    want = oracle.f64_to_bf16_bits(oracle.rope3d_bf16(inp.q[inp.video_rows], inp.pos,
+                                                      theta=10000.0, dims=(32, 48, 48)))
+    assert np.array_equal(bits(x), want)
+
+
+# ---------------------------------------------------------------- append ----
+
+def _adversarial_rows(n_rows, seed):
+    """bf16 rows whose quotients x/scale sit next to half-integers, plus zero
+    rows and rows whose scale is a power of two."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_rows, HEAD_DIM))
+    a = np.abs(x).max(axis=1)
+    scale = (a / 127.0).astype(np.float32).astype(np.float64)
+    k = rng.integers(-126, 126, size=(n_rows, HEAD_DIM)) + 0.5
+    near = k * scale[:, None] * (1.0 + rng.choice([-1, 1], size=k.shape) * 2.0 ** -20)
+    pick = rng.random((n_rows, HEAD_DIM)) < 0.5
+    x = np.where(pick, near, x)
+    x[np.arange(n_rows), np.argmax(np.abs(x), axis=1)] = a     # keep absmax
+    x[0] = 0.0
+    x[1, :] = 0.0
+    x[1, 0] = 127.0 * 2.0 ** -5
+    x[1, 1:6] = np.array([0.5, 1.5, 2.5, -2.5, 3.5]) * 2.0 ** -5
+    return oracle.f64_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("dtype", ["int8", "bf16"])
+def test_append_bit_exact_with_ring_wrap(dtype):
+    g, h, n_slots = 100, 3, 5
+    rows = _adversarial_rows(3 * g * h, 31).reshape(3 * g, h, HEAD_DIM)
+    vrows = workloads.normal_bf16(8, (3 * g, h, HEAD_DIM))
+    cache = sc.KVCache(n_slots, h, g, dtype, "cuda")
+    sc.kv_cache_append(cache, 3, _bf(rows), _bf(vrows))      # slots 3, 4, 0
+    torch.cuda.synchronize()
+    for f, slot in enumerate([3, 4, 0]):
+        kf = rows[f * g:(f + 1) * g].transpose(1, 0, 2)       # [h, g, D]
+        vf = vrows[f * g:(f + 1) * g].transpose(1, 0, 2)
+        if dtype == "int8":
+            kc, ks = oracle.quantise_int8(oracle.bf16_bits_to_f64(kf))
+            vc, vs = oracle.quantise_int8(oracle.bf16_bits_to_f64(vf))
+            assert np.array_equal(cache.k[slot].cpu().numpy(), kc)
+            assert np.array_equal(cache.k_scale[slot].cpu().numpy(), ks)
+            assert np.array_equal(cache.v[slot].cpu().numpy(), vc)
+            assert np.array_equal(cache.v_scale[slot].cpu().numpy(), vs)
+        else:
+            assert np.array_equal(bits(cache.k[slot]), kf)
+            assert np.array_equal(bits(cache.v[slot]), vf)
+    for slot in (1, 2):
+        assert not cache.k[slot].view(torch.uint8).cpu().numpy().any()
+
+
+# ------------------------------------------------------------- attention ----
+
+def _check_chain(name):
+    _say("chain", name)
+    inp = workloads.make_inputs(name)
+    cfg = inp.cfg
+    r = gpu_chain(inp)
+    # RoPE of current rows, bit-exact
+    q, k, _ = oracle_inputs(inp)
+    assert np.array_equal(bits(r.q), oracle.f64_to_bf16_bits(q))
+    assert np.array_equal(bits(r.k), oracle.f64_to_bf16_bits(k))
+    cache = None
+    if len(cfg.hist_t):
+        cache = oracle_cache(inp)
+        nf = len(cfg.hist_t)
+        if cfg.cache_dtype == "int8":
+            assert np.array_equal(r.cache.k[:nf].cpu().numpy(), cache[0])
+            assert np.array_equal(r.cache.v[:nf].cpu().numpy(), cache[1])
+            assert np.array_equal(r.cache.k_scale[:nf].cpu().numpy(), cache[2])
+            assert np.array_equal(r.cache.v_scale[:nf].cpu().numpy(), cache[3])
+        else:
+            assert np.array_equal(bits(r.cache.k[:nf]), oracle.f64_to_bf16_bits(cache[0]))
+        assert list(r.slots) == list(oracle.window_select(inp.slot_t, cfg.window))
+    o_ref, lse_ref = oracle_chain(inp, cache=cache)
+    mx, mean = attn_errors(to_f64(r.o), o_ref)
+    lerr = float(np.abs(r.lse.cpu().numpy() - lse_ref).max())
+    _say("  %s: max %.3e mean %.3e lse %.3e" % (name, mx, mean, lerr))
+    assert mx <= MAX_ERR and mean <= MEAN_ERR and lerr <= LSE_ERR
+    if cfg.append:
+        (start, tl, _), s = inp.segments[0], cfg.segments[0]
+        n = s.n_frames * cfg.tokens_per_frame
+        nf = len(cfg.hist_t)
+        g, h = cfg.tokens_per_frame, cfg.n_heads
+        kf = k[start + tl:start + tl + n].reshape(s.n_frames, g, h, HEAD_DIM).transpose(0, 2, 1, 3)
+        kc, ks = oracle.quantise_int8(kf)
+        assert np.array_equal(r.cache.k[nf:nf + s.n_frames].cpu().numpy(), kc)
+        assert np.array_equal(r.cache.k_scale[nf:nf + s.n_frames].cpu().numpy(), ks)
+        assert list(r.cache.slot_t[nf:nf + s.n_frames]) == list(range(s.t0, s.t0 + s.n_frames))
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_chain_small(name):
+    _check_chain(name)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_chain_full_size(name):
+    _check_chain(name)
+
+
+def test_attention_identical_int8_inputs_mid():
+    # attention alone on directly drawn INT8 cache bytes (no RoPE anywhere)
+    cfg = workloads.ALL["mid_int8"]
+    inp = workloads.make_inputs(cfg)
+    kc, vc, ks, vs = workloads.direct_int8_cache(cfg, cfg.n_slots)
+    cache = sc.KVCache(cfg.n_slots, cfg.n_heads, cfg.tokens_per_frame, "int8", "cuda")
+    cache.k.copy_(torch.from_numpy(kc))
+    cache.v.copy_(torch.from_numpy(vc))
+    cache.k_scale.copy_(torch.from_numpy(ks))
+    cache.v_scale.copy_(torch.from_numpy(vs))
+    slots = np.array([6, 2, 0, 7], dtype=np.int32)     # any order, any slots
+    o = sc.segcausal_joint_attn(_bf(inp.q), _bf(inp.k), _bf(inp.v), inp.segments, cfg.sm_scale,
+                                cache=cache, hist_slots=torch.from_numpy(slots).cuda())
+    hk, hv = oracle.history_keys(kc, vc, slots, ks, vs)
+    ref, _ = oracle.joint_attn(oracle.bf16_bits_to_f64(inp.q), oracle.bf16_bits_to_f64(inp.k),
+                               oracle.bf16_bits_to_f64(inp.v),
+                               [oracle.Segment(*s) for s in inp.segments], hk, hv, cfg.sm_scale)
+    mx, mean = attn_errors(to_f64(o), ref)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR, (mx, mean)
+
+
+def test_attention_deterministic_and_strided():
+    inp = workloads.make_inputs("c2")
+    cfg = inp.cfg
+    r = gpu_chain(inp, with_lse=False)
+    # same call again: bitwise identical (no races in the LDS pipeline)
+    hist = torch.from_numpy(r.slots).cuda()
+    o2 = sc.segcausal_joint_attn(r.q, r.k, r.v, inp.segments, cfg.sm_scale, cache=r.cache,
+                                 hist_slots=hist)
+    assert torch.equal(r.o, o2)
+    # q/k/v as views of one fused [n, 3, H, D] tensor, output into a strided view
+    qkv = torch.stack([r.q, r.k, r.v], dim=1)
+    out_buf = torch.zeros((cfg.n_cur, 2, cfg.n_heads, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    sc.segcausal_joint_attn(qkv[:, 0], qkv[:, 1], qkv[:, 2], inp.segments, cfg.sm_scale,
+                            cache=r.cache, hist_slots=hist, out=out_buf[:, 1])
+    torch.cuda.synchronize()
+    assert torch.equal(out_buf[:, 1], r.o)
+    assert not out_buf[:, 0].any()
+
+
+def test_packed_causality_on_gpu():
+    inp = workloads.make_inputs("c0_packed3")
+    cfg = inp.cfg
+    r = gpu_chain(inp, with_lse=False)
+    s2 = inp.segments[2][0]
+    q2, k2, v2 = r.q.clone(), r.k.clone(), r.v.clone()
+    for t in (q2, k2, v2):
+        t[s2:] = torch.randn_like(t[s2:]) * 4
+    o2 = sc.segcausal_joint_attn(q2, k2, v2, inp.segments, cfg.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o2[:s2], r.o[:s2])
+    assert not torch.equal(o2[s2:], r.o[s2:])
+
+
+def test_edge_shapes():
+    rng = np.random.default_rng(5)
+    # one query row, one segment of text only with a single valid key
+    for n_cur, seg in [(1, (0, 1, 1)), (3, (0, 3, 1)), (65, (0, 0, 0)), (300, (0, 299, 7))]:
+        qb = workloads.normal_bf16(11, (n_cur, 2, HEAD_DIM), 0.1)
+        kb = workloads.normal_bf16(12, (n_cur, 2, HEAD_DIM))
+        vb = workloads.normal_bf16(13, (n_cur, 2, HEAD_DIM))
+        o = sc.segcausal_joint_attn(_bf(qb), _bf(kb), _bf(vb), [seg], 1.0)
+        ref, _ = oracle.joint_attn(*(oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb)),
+                                   [oracle.Segment(*seg)], sm_scale=1.0)
+        mx, mean = attn_errors(to_f64(o), ref)
+        assert mx <= MAX_ERR and mean <= MEAN_ERR, (n_cur, seg, mx, mean)
+    # empty call writes nothing
+    z = torch.zeros((0, 2, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    sc.segcausal_joint_attn(z, z, z, [(0, 0, 0)], 1.0)
+
+
+# ----------------------------------------------------- c4 at full size ----
+
+def test_c4_append_and_rope_bit_exact():
+    cfg = workloads.CONFIGS["c4"]
+    _say("c4 append")
+    inp = workloads.make_inputs(cfg)
+    r = gpu_chain(inp, with_lse=False)
+    s = cfg.segments[0]
+    g, h = cfg.tokens_per_frame, cfg.n_heads
+    # current segment: RoPE bit-exact on sampled frames, append codes bit-exact
+    rng = np.random.default_rng(44)
+    frames = rng.choice(s.n_frames, size=6, replace=False)
+    for f in frames:
+        a = 256 + f * g
+        kf = oracle.rope3d_bf16(inp.k[a:a + g], inp.pos[f * g:(f + 1) * g])
+        assert np.array_equal(bits(r.k[a:a + g]), oracle.f64_to_bf16_bits(kf))
+        kc, ks = oracle.quantise_int8(kf.transpose(1, 0, 2))
+        vc, vs = oracle.quantise_int8(oracle.bf16_bits_to_f64(inp.v[a:a + g]).transpose(1, 0, 2))
+        slot = 288 + f
+        assert np.array_equal(r.cache.k[slot].cpu().numpy(), kc)
+        assert np.array_equal(r.cache.k_scale[slot].cpu().numpy(), ks)
+        assert np.array_equal(r.cache.v[slot].cpu().numpy(), vc)
+        assert np.array_equal(r.cache.v_scale[slot].cpu().numpy(), vs)
+    # history frames: sampled frames bit-exact
+    for f in rng.choice(288, size=6, replace=False):
+        kf = oracle.rope3d_bf16(inp.hist_k[f * g:(f + 1) * g], inp.hist_pos[f * g:(f + 1) * g])
+        kc, ks = oracle.quantise_int8(kf.transpose(1, 0, 2))
+        assert np.array_equal(r.cache.k[f].cpu().numpy(), kc)
+        assert np.array_equal(r.cache.k_scale[f].cpu().numpy(), ks)
+    # attention on sampled rows, reading the cache exactly as the oracle builds it
+    rows = np.concatenate([np.arange(0, 256, 4), 256 + rng.choice(cfg.n_video, 192, replace=False)])
+    _say("c4 oracle rows", len(rows))
+    o_ref = _c4_rows_oracle(inp, rows)
+    got = to_f64(r.o[torch.from_numpy(rows).cuda()])
+    mx, mean = attn_errors(got, o_ref)
+    _say("  c4 sampled: max %.3e mean %.3e" % (mx, mean))
+    assert mx <= MAX_ERR and mean <= MEAN_ERR
+
+
+def _c4_rows_oracle(inp, rows):
+    """Oracle attention for sampled c4 rows, building every input itself."""
+    cfg = inp.cfg
+    g, h = cfg.tokens_per_frame, cfg.n_heads
+    q, k, v = oracle_inputs(inp)
+    nf = len(cfg.hist_t)
+    hk = np.empty((nf * g, h, HEAD_DIM))
+    hv = np.empty((nf * g, h, HEAD_DIM))
+    for f0 in range(0, nf, 24):
+        f1 = min(nf, f0 + 24)
+        sl = slice(f0 * g, f1 * g)
+        kr = oracle.rope3d_bf16(inp.hist_k[sl], inp.hist_pos[sl])
+        kc, ks = oracle.quantise_int8(kr)
+        vc, vs = oracle.quantise_int8(oracle.bf16_bits_to_f64(inp.hist_v[sl]))
+        hk[sl] = oracle.dequantise_int8(kc, ks)
+        hv[sl] = oracle.dequantise_int8(vc, vs)
+    segs = [oracle.Segment(*s) for s in inp.segments]
+    o, _ = oracle.joint_attn_rows(q, k, v, segs, rows, hk, hv, cfg.sm_scale)
+    return o
