@@ -1,0 +1,231 @@
+"""Throughput of the segment-causal joint attention hot path on one MI355X.
+
+One step = one segment of one DiT layer: the 8 denoising layer-steps of the
+distilled sampler (each: RoPE of the current video Q and K, then joint
+attention over the INT8 history plus the current segment), then the window
+select and the INT8 append of the segment's K/V to the cache. Inputs are
+seeded synthetic tensors at the workload's shapes, resident in HBM before the
+timed region. Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+from workloads import HEAD_DIM  # noqa: E402
+
+METRIC = "attention TFLOP/s + video tokens/s per layer-step; % of MFMA/HBM roofline"
+DENOISE_STEPS = 8            # distilled sampler steps per segment
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+ATTN_KERNEL = "attn_kernel"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "attn_c4_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_source_hash():
+    with open(os.path.join(ROOT, "segment_causal_dit_amd", "csrc", "attn.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(cfg_name):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    try:
+        with open(PROFILE_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("attn_source_sha") != attn_source_hash() or s.get("workload") != cfg_name:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, n_rows=1024):
+    """The fp64 oracle's attention on a bounded sample of the workload: all
+    heads of n_rows random query rows against every key. History codes are
+    drawn directly (seeded), so no GPU result feeds the oracle."""
+    import oracle
+    h = cfg.n_heads
+    rng = np.random.default_rng(1234)
+    nf = cfg.window
+    kc, vc, ks, vs = workloads.uniform_int8_cache(cfg, nf)
+    hk, hv = oracle.history_keys(kc, vc, np.arange(nf), ks, vs)
+    del kc, vc
+    q, k, v = (oracle.bf16_bits_to_f64(x) for x in (inp.q, inp.k, inp.v))
+    rows = np.sort(rng.choice(cfg.n_cur, n_rows, replace=False))
+    segs = [oracle.Segment(*s) for s in inp.segments]
+    cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.joint_attn_rows(q, k, v, segs, rows, hk, hv, cfg.sm_scale, chunk=256, workers=cores)
+    dt = time.perf_counter() - t0
+    flops = 4 * HEAD_DIM * h * n_rows * (cfg.n_hist_rows + cfg.n_cur)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "attention of %d random query rows x %d heads over all %d keys "
+                      "(numpy float64, %d threads, %.1f s)"
+                      % (n_rows, h, cfg.n_hist_rows + cfg.n_cur, cores, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c4", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention would shard by heads; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import segment_causal_dit_amd as sc
+
+    cfg = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g, h = cfg.tokens_per_frame, cfg.n_heads
+    log("generating %s inputs" % cfg.name)
+    inp = workloads.make_inputs(cfg)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_pre, k_pre, v = bf(inp.q), bf(inp.k), bf(inp.v)
+    q, k = q_pre.clone(), k_pre.clone()
+    seg = cfg.segments[0]
+    tl = seg.text_len
+    n_vid = cfg.n_video
+    pos = torch.from_numpy(inp.pos).to(dev)
+    n_hist_frames = len(cfg.hist_t)
+    cache = None
+    if n_hist_frames:
+        cache = sc.KVCache(cfg.n_slots, h, g, cfg.cache_dtype, dev)
+        hk = bf(inp.hist_k)
+        sc.rope3d_apply(hk, torch.from_numpy(inp.hist_pos).to(dev))
+        sc.kv_cache_append(cache, 0, hk, bf(inp.hist_v))
+        cache.slot_t[:] = inp.slot_t
+        del hk
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = {k_: [] for k_ in ("rope", "attn", "append")}
+
+    def rec(name, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        ev[name].append((a, b))
+
+    def one_step():
+        slots = sc.window_select(cache.slot_t[:n_hist_frames], cfg.window) if cache else None
+        hist = torch.from_numpy(slots).to(dev, non_blocking=False) if cache else None
+        for _ in range(DENOISE_STEPS):
+            rec("rope", lambda: (sc.rope3d_apply(q_pre[tl:], pos, x_out=q[tl:]),
+                                 sc.rope3d_apply(k_pre[tl:], pos, x_out=k[tl:])))
+            rec("attn", lambda: sc.segcausal_joint_attn(q, k, v, [(0, tl, seg.text_valid)],
+                                                        cfg.sm_scale, cache=cache,
+                                                        hist_slots=hist, out=out))
+        if cache is not None and cfg.append:
+            rec("append", lambda: sc.kv_cache_append(cache, n_hist_frames, k[tl:], v[tl:]))
+
+    out = torch.empty_like(q)
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    for k_ in ev:
+        ev[k_].clear()
+    log("timing %d steps" % args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    def avg_ms(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return float(np.mean(xs)) if xs else 0.0
+
+    attn_ms, rope_ms, app_ms = avg_ms("attn"), avg_ms("rope"), avg_ms("append")
+    flops = cfg.flops()
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    step_tflops = DENOISE_STEPS * flops / (ms_step * 1e-3) / 1e12
+    vid_tok_s = DENOISE_STEPS * n_vid / (ms_step * 1e-3)
+    rope_bytes = 2 * 2 * n_vid * h * HEAD_DIM * 2           # q and k, read + write
+    app_bytes = n_vid * h * ((HEAD_DIM * 2 + HEAD_DIM + 4) * 2 if cfg.cache_dtype == "int8"
+                             else HEAD_DIM * 2 * 2 * 2)
+    log("attn %.3f ms (%.1f TFLOP/s, %.1f%% of bf16 peak)  rope q+k %.3f ms (%.0f GB/s)  "
+        "append %.3f ms (%.0f GB/s)  step %.2f ms"
+        % (attn_ms, attn_tflops, 100 * attn_tflops / PEAK_BF16_TFLOPS, rope_ms,
+           rope_bytes / (rope_ms * 1e-3) / 1e9 if rope_ms else 0, app_ms,
+           app_bytes / (app_ms * 1e-3) / 1e9 if app_ms else 0, ms_step))
+
+    traffic = measured_traffic(cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(step_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %d current queries (%d text + %d video) x %d heads x 128 over "
+                        "%d %s history keys + the current segment; 8 denoising layer-steps "
+                        "(RoPE q,k + attention) + window select + append per step"
+                        % (cfg.name, cfg.n_cur, tl, n_vid, h, cfg.n_hist_rows, cfg.cache_dtype),
+            "n_cur": cfg.n_cur, "n_hist_keys": cfg.n_hist_rows, "heads": h,
+            "head_dim": HEAD_DIM, "cache": cfg.cache_dtype,
+        },
+        "video_tokens_per_s_per_layer_step": round(vid_tok_s, 1),
+        "kernels_ms": {"attn": round(attn_ms, 4), "rope_qk": round(rope_ms, 4),
+                       "append": round(app_ms, 4)},
+        "hbm_frac": {"rope_qk": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                     if rope_ms else None,
+                     "append": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                     if app_ms else None},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        del q_pre, k_pre, q, k, v, out, cache
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(cfg, inp)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,43 +15,71 @@
 // query of segment s if it lies in segment s and is not a padded text row, or
 // if it is a video row of an earlier segment.
 //
-// Design (one workgroup = 4 waves = one (query tile, head)):
-//  * each wave owns 32*QG query rows; Q stays in registers as MFMA B operands;
+// Design (one workgroup = 8 waves = 256 query rows of one head, one
+// workgroup per CU, two waves per SIMD):
+//  * each wave owns 32 query rows; Q stays in registers as MFMA B operands;
+//  * waves 0-3 stage the K/V tiles, so each SIMD hosts one staging wave and
+//    one compute-only wave and the staging cost is shared by 256 queries;
 //  * key tiles of 64 rows are staged through LDS, double buffered: K row-major
-//    [key][d] (272-byte rows), V transposed [d][key'] (144-byte rows) so that
-//    both MFMA operands are single 16-byte LDS reads; global loads for tile
-//    t+1 are issued before tile t is computed;
+//    [key][d] (272-byte rows), V transposed [d][key'] (128-byte rows, 16-byte
+//    chunks XOR-swizzled by row) so that both MFMA operands are single
+//    16-byte LDS reads without bank conflicts;
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: keys land in accumulator
 //    registers and queries across lanes, so a row max needs only one
-//    cross-half exchange; O^T = V^T P^T reuses the S^T accumulators as the
-//    P operand directly (V^T is stored in the matching key order);
+//    cross-half exchange (v_permlane32_swap); O^T = V^T P^T takes the S^T
+//    accumulators as the P operand directly (V^T is stored in the matching
+//    key order);
+//  * software pipeline: the QK^T MFMAs of tile t+1 are issued before the
+//    softmax of tile t, so MFMA and VALU work of one wave overlap; K is
+//    prefetched two tiles ahead and V one tile ahead, with one barrier per tile;
+//  * each wave stages a 16-row group of a tile: with frames of a multiple of
+//    16 tokens a group never straddles a frame, so its base address is
+//    wave-uniform and lanes only add 32-bit offsets; rows past the end are
+//    clamped to the last valid row (finite data) and masked;
 //  * online softmax in base 2 with the rescale of O deferred until the running
 //    max grows by more than 2^8 (exact: the final division uses the same
 //    reference max);
 //  * INT8 history rows are dequantised to bf16(code * scale) while they are
 //    written to LDS, so the MFMA path is the same for both cache types;
 //  * masks are per tile: only tiles at a ragged end or with segment structure
-//    evaluate a per-element predicate from a 64-entry key table in LDS; tiles
-//    invisible to a whole wave are skipped; keys of later segments than the
-//    workgroup's last query are never loaded;
+//    evaluate a per-element predicate from a 64-entry key table in LDS; keys
+//    of later segments than the workgroup's last query are never loaded;
 //  * workgroup ids are remapped so that each XCD (dispatched round-robin)
 //    works through contiguous query tiles of the same head, sharing K/V in L2.
 #include "internal.h"
+
+// Tuning switches (compile time): waves per workgroup (4 or 8; waves 0-3
+// stage K/V tiles, any further waves only compute), minimum waves per SIMD the
+// register allocation must allow, and whether QK^T of the next tile is issued
+// ahead of the softmax of the current one.
+#ifndef SEGC_ATTN_NW
+#define SEGC_ATTN_NW 8
+#endif
+#ifndef SEGC_ATTN_WAVES_PER_SIMD
+#define SEGC_ATTN_WAVES_PER_SIMD 2
+#endif
+#ifndef SEGC_ATTN_PIPELINE
+#define SEGC_ATTN_PIPELINE 0
+#endif
 
 namespace segc {
 namespace {
 
 constexpr int D = 128;
 constexpr int BN = 64;                 // keys per tile
-constexpr int NW = 4;                  // waves per workgroup
+constexpr int NW = SEGC_ATTN_NW;       // waves per workgroup
 constexpr int NT = NW * 64;
-constexpr int KS = 136;                // LDS K row stride (bf16 elements)
-constexpr int VS = 72;                 // LDS V^T row stride (bf16 elements)
-constexpr int K_ELEMS = BN * KS;
-constexpr int V_ELEMS = D * VS;
-constexpr int BUF_BYTES = (K_ELEMS + V_ELEMS) * 2 + BN * 4;
+constexpr int NSTAGE = 4;              // waves that stage tiles (16 rows each)
+constexpr int BM = 32 * NW;            // query rows per workgroup
+constexpr int KS = 136;                // LDS K row stride (bf16 elements, 272 B)
+constexpr int K_BYTES = BN * KS * 2;   // 17408
+constexpr int V_BYTES = D * BN * 2;    // 16384: V^T rows of 64 keys
+constexpr int INFO_BYTES = BN * 4;
+constexpr int KBUF0 = 0;
+constexpr int VBUF0 = 2 * K_BYTES;
+constexpr int INFO0 = VBUF0 + 2 * V_BYTES;
+constexpr int LDS_BYTES = INFO0 + 2 * INFO_BYTES;
 constexpr float kTau = 8.0f;           // deferred-rescale threshold (log2 units)
-constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -67,6 +95,17 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// max / sum of x over lanes l and l ^ 32 (both outputs of the swap hold one
+// lane of each half, whichever way the halves move)
+__device__ inline float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Segment of current row r (scalar loop over at most kMaxSeg entries).
 __device__ inline int seg_of(const AttnParams& p, int r) {
   int s = 0;
@@ -74,127 +113,138 @@ __device__ inline int seg_of(const AttnParams& p, int r) {
   return s;
 }
 
-// Where the rows of one key tile come from (uniform across the workgroup).
-struct TileSrc {
+struct Tile {
   int hist;      // 1 = history rows, 0 = current rows
   int j0;        // first row (history row index or current row index)
-  int nvalid;    // rows [0, nvalid) exist; the rest are zero-filled
-  int f0, r0;    // history: frame of row j0 and row inside that frame
-  int slot0, slot1;
+  int nvalid;    // rows [0, nvalid) exist; later rows are clamped and masked
 };
 
-__device__ inline TileSrc tile_src(const AttnParams& p, int t, int cur_end) {
-  TileSrc ts;
+__device__ inline Tile tile_at(const AttnParams& p, int t, int cur_end) {
+  Tile tl;
   if (t < p.hist_tiles) {
-    ts.hist = 1;
-    ts.j0 = t * BN;
-    ts.nvalid = min(BN, p.n_hist_rows - ts.j0);
-    ts.f0 = ts.j0 / p.G;
-    ts.r0 = ts.j0 - ts.f0 * p.G;
-    const int n_hist = p.n_hist_rows / p.G;
-    ts.slot0 = p.hist_slots[ts.f0];
-    ts.slot1 = (ts.f0 + 1 < n_hist) ? p.hist_slots[ts.f0 + 1] : ts.slot0;
+    tl.hist = 1;
+    tl.j0 = t * BN;
+    tl.nvalid = min(BN, p.n_hist_rows - tl.j0);
   } else {
-    ts.hist = 0;
-    ts.j0 = (t - p.hist_tiles) * BN;
-    ts.nvalid = min(BN, cur_end - ts.j0);
-    ts.f0 = ts.r0 = ts.slot0 = ts.slot1 = 0;
+    tl.hist = 0;
+    tl.j0 = (t - p.hist_tiles) * BN;
+    tl.nvalid = min(BN, cur_end - tl.j0);
   }
-  return ts;
+  return tl;
 }
 
-// Cache row index (in units of 128 elements) of history tile row o.
-__device__ inline int64_t hist_row(const AttnParams& p, const TileSrc& ts, int head, int o) {
-  int rr = ts.r0 + o;
-  int slot;
-  if (p.G >= BN) {
-    const bool nx = rr >= p.G;
-    slot = nx ? ts.slot1 : ts.slot0;
-    rr = nx ? rr - p.G : rr;
-  } else {
-    int f = ts.f0;
-    while (rr >= p.G) {
-      rr -= p.G;
-      ++f;
-    }
-    slot = p.hist_slots[f];
-  }
-  return ((int64_t)slot * p.n_heads + head) * p.G + rr;
+__device__ inline bool tile_masked(const AttnParams& p, const Tile& tl) {
+  return tl.nvalid < BN || (!tl.hist && p.needs_mask);
 }
 
-// Registers holding one tile's global loads between issue and LDS write.
-struct Stage {
-  u32x4 k[4];
-  u32x4 v[4];
-  float ks[2];
-  float vs[4];
+// Where a wave's 16-row group of a tile lives. Uniform fields describe the
+// group's first row; lanes add row offsets (clamped to `lim`).
+struct Group {
+  int64_t row0;   // history: cache row index of the group's first row; current: row index
+  int lim;        // largest valid local row (0..15)
+  bool generic;   // history frames not a multiple of 16 tokens: per-lane rows
+  int j;          // first tile row of the group (generic path)
 };
 
-__device__ inline void issue_loads(const AttnParams& p, const TileSrc& ts, int head, int tid,
-                                   Stage& st) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  const int quad = tid & 15, c8 = tid >> 4;
-  if (!ts.hist || !p.hist_int8) {
-    // bf16 rows: K as 16-byte chunks (16 lanes per row), V as 4 rows x 8 d
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NT * i;
-      const int o = c >> 4, col = c & 15;
-      st.k[i] = z;
-      if (o < ts.nvalid) {
-        const uint16_t* src = ts.hist
-            ? (const uint16_t*)p.hk + hist_row(p, ts, head, o) * D
-            : p.k + (int64_t)(ts.j0 + o) * p.k_st + head * p.k_sh;
-        st.k[i] = *(const u32x4*)(src + col * 8);
-      }
+__device__ inline Group group_at(const AttnParams& p, const Tile& tl, int w, int head) {
+  Group g;
+  const int last = tl.j0 + tl.nvalid - 1;            // last valid row of the tile
+  const int gs = min(tl.j0 + 16 * w, last & ~15);
+  g.lim = last - gs;
+  g.generic = false;
+  g.j = gs;
+  if (tl.hist) {
+    if (p.G % 16 == 0) {
+      const int f = gs / p.G;
+      const int slot = p.hist_slots[f];
+      g.row0 = ((int64_t)slot * p.n_heads + head) * p.G + (gs - f * p.G);
+    } else {
+      g.generic = true;
+      g.row0 = 0;
     }
+  } else {
+    g.row0 = gs;
+  }
+  return g;
+}
+
+// Cache row index of local row lr of a history group (generic path: per lane).
+__device__ inline int64_t hist_row_generic(const AttnParams& p, const Group& g, int lr, int head) {
+  const int row = g.j + lr;
+  const int f = row / p.G;
+  const int slot = p.hist_slots[f];
+  return ((int64_t)slot * p.n_heads + head) * p.G + (row - f * p.G);
+}
+
+struct KStage { u32x4 d[4]; float s[2]; };
+struct VStage { u32x4 d[4]; float s[4]; };
+
+// ---- K: 4 instructions x (4 rows x 16 chunks of 16 B) = 16 rows per wave
+__device__ inline void load_k(const AttnParams& p, const Tile& tl, int w, int lane, int head,
+                              KStage& st) {
+  const Group g = group_at(p, tl, w, head);
+  if (!tl.hist || !p.hist_int8) {
+    const int ch = lane & 15;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int o = quad * 4 + r;
-      st.v[r] = z;
-      if (o < ts.nvalid) {
-        const uint16_t* src = ts.hist
-            ? (const uint16_t*)p.hv + hist_row(p, ts, head, o) * D
-            : p.v + (int64_t)(ts.j0 + o) * p.v_st + head * p.v_sh;
-        st.v[r] = *(const u32x4*)(src + c8 * 8);
+      const int lr = min(4 * r + (lane >> 4), g.lim);
+      const char* src;
+      if (!tl.hist) {
+        const char* base = (const char*)(p.k + g.row0 * p.k_st + head * p.k_sh);
+        src = base + (uint32_t)(lr * (int)p.k_st * 2);
+      } else if (!g.generic) {
+        const char* base = (const char*)p.hk + g.row0 * 256;
+        src = base + (uint32_t)(lr * 256);
+      } else {
+        src = (const char*)p.hk + hist_row_generic(p, g, lr, head) * 256;
       }
+      st.d[r] = *(const u32x4*)(src + ch * 16);
     }
   } else {
-    // int8 history rows: K as 16-code chunks (8 lanes per row), V as 4 rows x 8 codes
+    const int c16 = lane & 7;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + NT * i;
-      const int o = c >> 3, col = c & 7;
-      st.k[i] = z;
-      st.ks[i] = 0.0f;
-      if (o < ts.nvalid) {
-        const int64_t row = hist_row(p, ts, head, o);
-        st.k[i] = *(const u32x4*)((const int8_t*)p.hk + row * D + col * 16);
-        st.ks[i] = p.hks[row];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int o = quad * 4 + r;
-      st.v[r] = z;
-      st.vs[r] = 0.0f;
-      if (o < ts.nvalid) {
-        const int64_t row = hist_row(p, ts, head, o);
-        const u32x2 w = *(const u32x2*)((const int8_t*)p.hv + row * D + c8 * 8);
-        st.v[r].x = w.x;
-        st.v[r].y = w.y;
-        st.vs[r] = p.hvs[row];
-      }
+      const int lr = min(8 * i + (lane >> 3), g.lim);
+      const int64_t row = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
+      st.d[i] = *(const u32x4*)((const char*)p.hk + row * 128 + c16 * 16);
+      st.s[i] = p.hks[row];
     }
   }
 }
 
-// Offset (keys) of the 4 consecutive keys 4*quad..4*quad+3 inside a V^T row.
-// Within each 16-key chunk, key bits 2 and 3 are swapped so that the 8 keys a
-// lane half feeds to one PV MFMA are contiguous.
-__device__ inline int vt_pos(int quad) {
-  const int m = quad & 3;
-  return (quad >> 2) * 16 + (((m & 1) << 1) | (m >> 1)) * 4;
+// ---- V: lane holds 4 consecutive rows (quad) x 8 elements (chunk c8)
+__device__ inline void load_v(const AttnParams& p, const Tile& tl, int w, int lane, int head,
+                              VStage& st) {
+  const Group g = group_at(p, tl, w, head);
+  const int q4 = 4 * (lane >> 4);
+  const int c8 = lane & 15;
+  if (!tl.hist || !p.hist_int8) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int lr = min(q4 + r, g.lim);
+      const char* src;
+      if (!tl.hist) {
+        const char* base = (const char*)(p.v + g.row0 * p.v_st + head * p.v_sh);
+        src = base + (uint32_t)(lr * (int)p.v_st * 2);
+      } else if (!g.generic) {
+        const char* base = (const char*)p.hv + g.row0 * 256;
+        src = base + (uint32_t)(lr * 256);
+      } else {
+        src = (const char*)p.hv + hist_row_generic(p, g, lr, head) * 256;
+      }
+      st.d[r] = *(const u32x4*)(src + c8 * 16);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int lr = min(q4 + r, g.lim);
+      const int64_t row = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
+      const u32x2 w2 = *(const u32x2*)((const char*)p.hv + row * 128 + c8 * 8);
+      st.d[r].x = w2.x;
+      st.d[r].y = w2.y;
+      st.s[r] = p.hvs[row];
+    }
+  }
 }
 
 // int8 code bytes (4 per dword) times scale -> fp32; (u - 128) * s in one fma.
@@ -207,90 +257,194 @@ __device__ inline void dequant4(uint32_t w, float s, float* out) {
   out[3] = fmaf((float)(u >> 24), s, ms);
 }
 
-__device__ inline void write_lds(const AttnParams& p, const TileSrc& ts, int tid, const Stage& st,
-                                 char* buf, bool need_info, int cur_end) {
-  uint16_t* Kl = (uint16_t*)buf;
-  uint16_t* Vl = Kl + K_ELEMS;
-  int* info = (int*)(Vl + V_ELEMS);
-  const int quad = tid & 15, c8 = tid >> 4;
-  const int vp = vt_pos(quad);
-  if (!ts.hist || !p.hist_int8) {
+__device__ inline void store_k(const AttnParams& p, const Tile& tl, int w, int lane,
+                               const KStage& st, char* kbuf) {
+  if (!tl.hist || !p.hist_int8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + NT * i;
-      *(u32x4*)(Kl + (c >> 4) * KS + (c & 15) * 8) = st.k[i];
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int w = dd >> 1;
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 o2;
-      o2.x = __builtin_amdgcn_perm(st.v[1][w], st.v[0][w], sel);
-      o2.y = __builtin_amdgcn_perm(st.v[3][w], st.v[2][w], sel);
-      *(u32x2*)(Vl + (c8 * 8 + dd) * VS + vp) = o2;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * w + 4 * r + (lane >> 4);
+      *(u32x4*)(kbuf + row * (KS * 2) + (lane & 15) * 16) = st.d[r];
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + NT * i;
-      const int o = c >> 3, col = c & 7;
+      const int row = 16 * w + 8 * i + (lane >> 3);
       float f[16];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) dequant4(st.k[i][w], st.ks[i], f + 4 * w);
+      for (int e = 0; e < 4; ++e) dequant4(st.d[i][e], st.s[i], f + 4 * e);
       u32x4 a, b;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         a[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
-        b[e] = pack_bf16(f[8 + 2 * e], f[8 + 2 * e + 1]);
+        b[e] = pack_bf16(f[8 + 2 * e], f[9 + 2 * e]);
       }
-      *(u32x4*)(Kl + o * KS + col * 16) = a;
-      *(u32x4*)(Kl + o * KS + col * 16 + 8) = b;
+      char* dst = kbuf + row * (KS * 2) + (lane & 7) * 32;
+      *(u32x4*)dst = a;
+      *(u32x4*)(dst + 16) = b;
     }
+  }
+}
+
+// V^T byte offset of (row d, keys pos..pos+3) with pos a multiple of 4. Keys
+// are stored with bits 2 and 3 of their index inside each 16-key chunk
+// swapped (pos), and the row's 16-byte chunks XOR-swizzled by (d ^ d>>3) & 7.
+__device__ inline int vt_off(int d, int pos) {
+  const int sw = (d ^ (d >> 3)) & 7;
+  return d * (BN * 2) + ((((pos >> 3) ^ sw) << 4) | ((pos & 4) << 1));
+}
+
+// Position of the 4 keys 4*quad..4*quad+3 inside a V^T row.
+__device__ inline int vt_pos(int quad) {
+  const int m = quad & 3;
+  return (quad >> 2) * 16 + (((m & 1) << 1) | (m >> 1)) * 4;
+}
+
+__device__ inline void store_v(const AttnParams& p, const Tile& tl, int w, int lane,
+                               const VStage& st, char* vbuf) {
+  const int quad = 4 * w + (lane >> 4);
+  const int c8 = lane & 15;
+  const int pos = vt_pos(quad);
+  if (!tl.hist || !p.hist_int8) {
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const int e = dd >> 1;
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 o2;
+      o2.x = __builtin_amdgcn_perm(st.d[1][e], st.d[0][e], sel);
+      o2.y = __builtin_amdgcn_perm(st.d[3][e], st.d[2][e], sel);
+      *(u32x2*)(vbuf + vt_off(8 * c8 + dd, pos)) = o2;
+    }
+  } else {
     float f[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      dequant4(st.v[r].x, st.vs[r], f[r]);
-      dequant4(st.v[r].y, st.vs[r], f[r] + 4);
+      dequant4(st.d[r].x, st.s[r], f[r]);
+      dequant4(st.d[r].y, st.s[r], f[r] + 4);
     }
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
       u32x2 o2;
       o2.x = pack_bf16(f[0][dd], f[1][dd]);
       o2.y = pack_bf16(f[2][dd], f[3][dd]);
-      *(u32x2*)(Vl + (c8 * 8 + dd) * VS + vp) = o2;
+      *(u32x2*)(vbuf + vt_off(8 * c8 + dd, pos)) = o2;
     }
-  }
-  if (need_info && tid < BN) {
-    // [lo, hi] range of query segments that may see key tid; lo > hi = nobody
-    int lo = 0xFFFF, hi = 0;
-    if (tid < ts.nvalid) {
-      if (ts.hist) {
-        lo = 0;
-        hi = 0xFFFF;
-      } else {
-        const int jc = ts.j0 + tid;
-        if (jc < cur_end) {
-          const int s = seg_of(p, jc);
-          const int ti = jc - p.seg_start[s];
-          if (ti >= p.seg_text_len[s]) {
-            lo = s;
-            hi = 0xFFFF;
-          } else if (ti < p.seg_text_valid[s]) {
-            lo = s;
-            hi = s;
-          }
-        }
-      }
-    }
-    info[tid] = lo | (hi << 16);
   }
 }
 
-template <int QG>
-__global__ __launch_bounds__(NT, 1) void attn_kernel(AttnParams p) {
+// Visibility table of the tile's 64 keys: [lo, hi] range of query segments
+// that may see the key (lo > hi: nobody).
+__device__ inline void store_info(const AttnParams& p, const Tile& tl, int tid, int* info) {
+  if (tid >= BN) return;
+  int lo = 0xFFFF, hi = 0;
+  if (tid < tl.nvalid) {
+    if (tl.hist) {
+      lo = 0;
+      hi = 0xFFFF;
+    } else {
+      const int jc = tl.j0 + tid;
+      const int s = seg_of(p, jc);
+      const int ti = jc - p.seg_start[s];
+      if (ti >= p.seg_text_len[s]) {
+        lo = s;
+        hi = 0xFFFF;
+      } else if (ti < p.seg_text_valid[s]) {
+        lo = s;
+        hi = s;
+      }
+    }
+  }
+  info[tid] = lo | (hi << 16);
+}
+
+// S^T (64 keys x 32 queries) = K Q^T from the K tile in LDS.
+__device__ inline void qk_tile(const char* kbuf, const bf16x8 (&qf)[8], int lr, int hh,
+                               f32x16 (&s)[2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const char* row = kbuf + (32 * kb + lr) * (KS * 2) + hh * 16;
+    bf16x8 a = *(const bf16x8*)row;
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int dt = 1; dt < 8; ++dt) {
+      a = *(const bf16x8*)(row + dt * 32);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dt], s[kb], 0, 0, 0);
+    }
+  }
+}
+
+struct RowState {
+  float m, l;
+};
+
+// Softmax of one tile (in place: s becomes p) and O rescale when needed.
+__device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info, int qseg, int hh,
+                                    float c, RowState& rs, f32x16 (&o)[4]) {
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const i32x4 inf4 = *(const i32x4*)(info + 32 * kb + 8 * jq + 4 * hh);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int lo = inf4[jj] & 0xFFFF, hi = (inf4[jj] >> 16) & 0xFFFF;
+          if (qseg < lo || qseg > hi) s[kb][4 * jq + jj] = -INFINITY;
+        }
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+  mx = xhalf_max(mx);
+  const float mnew = fmaxf(rs.m, mx);
+  const bool need = (mnew - rs.m) * c > kTau;          // false for -inf/-inf (NaN)
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float alpha = __builtin_amdgcn_exp2f((rs.m - mnew) * c);
+    rs.m = mnew;
+    rs.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+  }
+  const float mc = (rs.m == -INFINITY) ? 0.0f : rs.m * c;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][j], c, -mc));
+}
+
+// O^T += V^T P^T for one tile; the row sum l accumulates the fp32 P values.
+__device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lr, int hh,
+                               f32x16 (&o)[4], RowState& rs) {
+  float ls = 0.0f;
+#pragma unroll
+  for (int ck = 0; ck < 4; ++ck) {
+    u32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = pack_bf16(s[ck >> 1][8 * (ck & 1) + 2 * e], s[ck >> 1][8 * (ck & 1) + 2 * e + 1]);
+      ls += s[ck >> 1][8 * (ck & 1) + 2 * e] + s[ck >> 1][8 * (ck & 1) + 2 * e + 1];
+    }
+    const bf16x8 pb = as_bf16x8(u);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 32 * db + lr;
+      const int sw = (d ^ (d >> 3)) & 7;
+      const bf16x8 a = *(const bf16x8*)(vbuf + d * (BN * 2) + (((2 * ck + hh) ^ sw) << 4));
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+    }
+  }
+  rs.l += ls;
+}
+
+__global__ __launch_bounds__(NT, SEGC_ATTN_WAVES_PER_SIMD) void attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
 
   // XCD-aware remap: hardware deals workgroup b to XCD b % 8; give each XCD a
@@ -302,204 +456,158 @@ __global__ __launch_bounds__(NT, 1) void attn_kernel(AttnParams p) {
   const int head = logical / p.n_qtiles;
   const int qtile = logical - head * p.n_qtiles;
 
-  constexpr int BM = 32 * QG * NW;
   const int m0 = qtile * BM;
   const int wg_last = min(m0 + BM, p.n_cur) - 1;
   const int cur_end = p.seg_start[seg_of(p, wg_last) + 1];   // later keys are future for all
   const int n_tiles = p.hist_tiles + (cur_end + BN - 1) / BN;
 
-  const int w0 = m0 + wave * 32 * QG;
-  const bool wave_live = w0 < p.n_cur;
-  const int w_last = min(w0 + 32 * QG, p.n_cur) - 1;
-  const int w_vis_end = wave_live ? p.seg_start[seg_of(p, w_last) + 1] : 0;
-
-  // Q operands and per-row segment
-  bf16x8 qf[QG][8];
-  int qs[QG];
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const int row = w0 + 32 * g + lr;
-    const bool ok = row < p.n_cur;
-    qs[g] = seg_of(p, ok ? row : p.n_cur - 1);
-    const uint16_t* src = p.q + (int64_t)(ok ? row : 0) * p.q_st + head * p.q_sh + hh * 8;
+  // Q operands (B of S^T = K Q^T) and the query row's segment
+  const int qrow = m0 + 32 * w + lr;
+  const bool qok = qrow < p.n_cur;
+  const int qseg = seg_of(p, qok ? qrow : p.n_cur - 1);
+  bf16x8 qf[8];
+  {
+    const uint16_t* src = p.q + (int64_t)(qok ? qrow : 0) * p.q_st + head * p.q_sh + hh * 8;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       u32x4 u = {0u, 0u, 0u, 0u};
-      if (ok) u = *(const u32x4*)(src + 16 * t);
-      qf[g][t] = as_bf16x8(u);
+      if (qok) u = *(const u32x4*)(src + 16 * t);
+      qf[t] = as_bf16x8(u);
     }
   }
 
-  f32x16 oacc[4][QG];
-  float mrow[QG], lrow[QG];
+  f32x16 o[4];
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    mrow[g] = -INFINITY;
-    lrow[g] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[db][g][j] = 0.0f;
-  }
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  RowState rs = {-INFINITY, 0.0f};
   const float c = p.scale_log2;
 
-  auto tile_needs_info = [&](const TileSrc& ts) -> bool {
-    return ts.nvalid < BN || (!ts.hist && p.needs_mask);
+  const bool stager = w < NSTAGE;
+#if SEGC_ATTN_PIPELINE
+  // prologue: K(0), V(0) (+ key table), K(1) into LDS
+  if (stager) {
+    KStage ks;
+    VStage vs;
+    const Tile t0 = tile_at(p, 0, cur_end);
+    load_k(p, t0, w, lane, head, ks);
+    load_v(p, t0, w, lane, head, vs);
+    store_k(p, t0, w, lane, ks, smem + KBUF0);
+    store_v(p, t0, w, lane, vs, smem + VBUF0);
+    if (tile_masked(p, t0)) store_info(p, t0, tid, (int*)(smem + INFO0));
+    if (n_tiles > 1) {
+      const Tile t1 = tile_at(p, 1, cur_end);
+      load_k(p, t1, w, lane, head, ks);
+      store_k(p, t1, w, lane, ks, smem + KBUF0 + K_BYTES);
+    }
+  }
+  __syncthreads();
+
+  f32x16 sa[2], sb[2];
+  qk_tile(smem + KBUF0, qf, lr, hh, sa);
+
+  // one pipelined tile: S(t+1) into s_next while s_cur (tile t) is consumed
+  auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    const bool has_v1 = t + 1 < n_tiles;
+    const bool has_k2 = t + 2 < n_tiles;
+    const Tile tt = tile_at(p, t, cur_end);
+    KStage ks;
+    VStage vs;
+    const Tile tk = tile_at(p, t + 2, cur_end);
+    const Tile tv = tile_at(p, t + 1, cur_end);
+    if (has_k2 && stager) load_k(p, tk, w, lane, head, ks);
+    if (has_v1) {
+      if (stager) load_v(p, tv, w, lane, head, vs);
+      qk_tile(smem + KBUF0 + ((t + 1) & 1) * K_BYTES, qf, lr, hh, s_next);
+    }
+    softmax_tile(s_cur, tile_masked(p, tt), (const int*)(smem + INFO0 + (t & 1) * INFO_BYTES), qseg,
+                 hh, c, rs, o);
+    pv_tile(smem + VBUF0 + (t & 1) * V_BYTES, s_cur, lr, hh, o, rs);
+    if (stager) {
+      if (has_k2) store_k(p, tk, w, lane, ks, smem + KBUF0 + (t & 1) * K_BYTES);
+      if (has_v1) {
+        store_v(p, tv, w, lane, vs, smem + VBUF0 + ((t + 1) & 1) * V_BYTES);
+        if (tile_masked(p, tv))
+          store_info(p, tv, tid, (int*)(smem + INFO0 + ((t + 1) & 1) * INFO_BYTES));
+      }
+    }
+    __syncthreads();
   };
 
-  Stage st;
-  TileSrc ts_next = tile_src(p, 0, cur_end);
-  issue_loads(p, ts_next, head, tid, st);
-  write_lds(p, ts_next, tid, st, smem, tile_needs_info(ts_next), cur_end);
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < n_tiles) step(t, sa, sb);
+#else
+  // prologue: tile 0 into LDS buffer 0
+  if (stager) {
+    KStage ks;
+    VStage vs;
+    const Tile t0 = tile_at(p, 0, cur_end);
+    load_k(p, t0, w, lane, head, ks);
+    load_v(p, t0, w, lane, head, vs);
+    store_k(p, t0, w, lane, ks, smem + KBUF0);
+    store_v(p, t0, w, lane, vs, smem + VBUF0);
+    if (tile_masked(p, t0)) store_info(p, t0, tid, (int*)(smem + INFO0));
+  }
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
-    const TileSrc ts = ts_next;
-    const bool have_next = t + 1 < n_tiles;
-    if (have_next) {
-      ts_next = tile_src(p, t + 1, cur_end);
-      issue_loads(p, ts_next, head, tid, st);
+    const bool has_next = t + 1 < n_tiles;
+    const Tile tt = tile_at(p, t, cur_end);
+    const Tile tn = tile_at(p, t + 1, cur_end);
+    KStage ks;
+    VStage vs;
+    if (has_next && stager) {
+      load_k(p, tn, w, lane, head, ks);
+      load_v(p, tn, w, lane, head, vs);
     }
-    char* buf = smem + (t & 1) * BUF_BYTES;
-    const bool skip = !wave_live || (!ts.hist && ts.j0 >= w_vis_end);
-    if (!skip) {
-      const uint16_t* Kl = (const uint16_t*)buf;
-      const uint16_t* Vl = Kl + K_ELEMS;
-      const int* info = (const int*)(Vl + V_ELEMS);
-
-      f32x16 sacc[2][QG];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < QG; ++g)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sacc[kb][g][j] = 0.0f;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *(const bf16x8*)(Kl + (32 * kb + lr) * KS + 16 * dt + 8 * hh);
-#pragma unroll
-          for (int g = 0; g < QG; ++g)
-            sacc[kb][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[g][dt], sacc[kb][g], 0, 0, 0);
-        }
-      }
-
-      if (tile_needs_info(ts)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const i32x4 inf4 = *(const i32x4*)(info + 32 * kb + 8 * jq + 4 * hh);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int lo = inf4[jj] & 0xFFFF, hi = (inf4[jj] >> 16) & 0xFFFF;
-#pragma unroll
-              for (int g = 0; g < QG; ++g)
-                if (qs[g] < lo || qs[g] > hi) sacc[kb][g][4 * jq + jj] = -INFINITY;
-            }
-          }
-      }
-
-#pragma unroll
-      for (int g = 0; g < QG; ++g) {
-        float mx = sacc[0][g][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][g][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrow[g], mx);
-        const bool need = (mnew - mrow[g]) * c > kTau;   // false for -inf/-inf (NaN)
-        if (__ballot(need)) {
-          const float alpha = __builtin_amdgcn_exp2f((mrow[g] - mnew) * c);
-          mrow[g] = mnew;
-          lrow[g] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[db][g][j] *= alpha;
-        }
-        const float mc = (mrow[g] == -INFINITY) ? 0.0f : mrow[g] * c;
-        float ls = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[kb][g][j], c, -mc));
-            sacc[kb][g][j] = e;
-            ls += e;
-          }
-        lrow[g] += ls;
-      }
-
-#pragma unroll
-      for (int ck = 0; ck < 4; ++ck) {
-        bf16x8 pb[QG];
-#pragma unroll
-        for (int g = 0; g < QG; ++g) {
-          u32x4 u;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            u[e] = pack_bf16(sacc[ck >> 1][g][8 * (ck & 1) + 2 * e],
-                             sacc[ck >> 1][g][8 * (ck & 1) + 2 * e + 1]);
-          pb[g] = as_bf16x8(u);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8 a = *(const bf16x8*)(Vl + (32 * db + lr) * VS + 16 * ck + 8 * hh);
-#pragma unroll
-          for (int g = 0; g < QG; ++g)
-            oacc[db][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[g], oacc[db][g], 0, 0, 0);
-        }
-      }
+    const int b = t & 1;
+    f32x16 sc[2];
+    qk_tile(smem + KBUF0 + b * K_BYTES, qf, lr, hh, sc);
+    softmax_tile(sc, tile_masked(p, tt), (const int*)(smem + INFO0 + b * INFO_BYTES), qseg, hh, c,
+                 rs, o);
+    pv_tile(smem + VBUF0 + b * V_BYTES, sc, lr, hh, o, rs);
+    if (has_next && stager) {
+      store_k(p, tn, w, lane, ks, smem + KBUF0 + (b ^ 1) * K_BYTES);
+      store_v(p, tn, w, lane, vs, smem + VBUF0 + (b ^ 1) * V_BYTES);
+      if (tile_masked(p, tn)) store_info(p, tn, tid, (int*)(smem + INFO0 + (b ^ 1) * INFO_BYTES));
     }
-    if (have_next)
-      write_lds(p, ts_next, tid, st, smem + ((t + 1) & 1) * BUF_BYTES, tile_needs_info(ts_next),
-                cur_end);
     __syncthreads();
   }
+#endif
 
   // epilogue: O = acc / l, bf16; lse = m * sm_scale + ln l
+  const float lt = xhalf_sum(rs.l);
+  const float inv = 1.0f / lt;
+  if (qok) {
+    uint16_t* dst = p.o + (int64_t)qrow * p.o_st + head * p.o_sh + 4 * hh;
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    const float lt = lrow[g] + __shfl_xor(lrow[g], 32);
-    const float inv = 1.0f / lt;
-    const int row = w0 + 32 * g + lr;
-    if (row < p.n_cur) {
-      uint16_t* dst = p.o + (int64_t)row * p.o_st + head * p.o_sh + 4 * hh;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          u32x2 w;
-          w.x = pack_bf16(oacc[db][g][4 * jq] * inv, oacc[db][g][4 * jq + 1] * inv);
-          w.y = pack_bf16(oacc[db][g][4 * jq + 2] * inv, oacc[db][g][4 * jq + 3] * inv);
-          *(u32x2*)(dst + 32 * db + 8 * jq) = w;
-        }
-      if (p.lse && hh == 0) p.lse[(int64_t)head * p.n_cur + row] = mrow[g] * p.sm_scale + logf(lt);
-    }
+      for (int jq = 0; jq < 4; ++jq) {
+        u32x2 v2;
+        v2.x = pack_bf16(o[db][4 * jq] * inv, o[db][4 * jq + 1] * inv);
+        v2.y = pack_bf16(o[db][4 * jq + 2] * inv, o[db][4 * jq + 3] * inv);
+        *(u32x2*)(dst + 32 * db + 8 * jq) = v2;
+      }
+    if (p.lse && hh == 0) p.lse[(int64_t)head * p.n_cur + qrow] = rs.m * p.sm_scale + logf(lt);
   }
-}
-
-template <int QG>
-hipError_t launch_qg(const AttnParams& p0, hipStream_t s) {
-  AttnParams p = p0;
-  constexpr int BM = 32 * QG * NW;
-  p.n_qtiles = (p.n_cur + BM - 1) / BM;
-  const int64_t nwg = (int64_t)p.n_qtiles * p.n_heads;
-  // more than 64 KB of dynamic LDS must be allowed explicitly (gfx950 has 160 KB per CU)
-  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<QG>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 2 * BUF_BYTES);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_kernel<QG>, dim3((unsigned)nwg), dim3(NT), 2 * BUF_BYTES, s, p);
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  return launch_qg<1>(p, s);
+hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
+  AttnParams p = p0;
+  p.n_qtiles = (p.n_cur + BM - 1) / BM;
+  const int64_t nwg = (int64_t)p.n_qtiles * p.n_heads;
+  // more than 64 KB of dynamic LDS must be allowed explicitly (gfx950 has 160 KB per CU)
+  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace segc

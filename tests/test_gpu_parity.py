@@ -246,6 +246,7 @@ def test_edge_shapes():
 
 # ----------------------------------------------------- c4 at full size ----
 
+@pytest.mark.timeout(900)
 def test_c4_append_and_rope_bit_exact():
     cfg = workloads.CONFIGS["c4"]
     _say("c4 append")

@@ -245,3 +245,15 @@ def direct_int8_cache(cfg, frames):
     kc = codes()
     vc = codes()
     return kc, vc, scales(), scales()
+
+
+def uniform_int8_cache(cfg, frames):
+    """Like direct_int8_cache but with codes uniform in [-127, 127] (a fast
+    draw for timing runs). Returns (k_codes, v_codes, k_scale, v_scale)."""
+    rng = np.random.Generator(np.random.PCG64(SEED + 6))
+    shape = (frames, cfg.n_heads, cfg.tokens_per_frame, HEAD_DIM)
+    kc = rng.integers(-127, 128, size=shape, dtype=np.int8)
+    vc = rng.integers(-127, 128, size=shape, dtype=np.int8)
+    ks = ((1.0 + rng.random(shape[:3])) / 64.0).astype(np.float32)
+    vs = ((1.0 + rng.random(shape[:3])) / 64.0).astype(np.float32)
+    return kc, vc, ks, vs
