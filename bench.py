@@ -31,7 +31,6 @@ DENOISE_STEPS = 8            # distilled sampler steps per segment
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 ATTN_KERNEL = "attn_kernel"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "attn_c4_counters.json")
 
 
 def log(*a):
@@ -47,7 +46,7 @@ def measured_traffic(cfg_name):
     """HBM bytes per attention launch from the committed counter summary, or
     None when it is missing or was taken on a different kernel source."""
     try:
-        with open(PROFILE_SUMMARY) as f:
+        with open(os.path.join(ROOT, "profiles", "attn_%s_counters.json" % cfg_name)) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
@@ -82,6 +81,84 @@ def cpu_baseline(cfg, inp, n_rows=1024):
                       % (n_rows, h, cfg.n_hist_rows + cfg.n_cur, cores, dt)}
 
 
+COPY_BYTES = 1 << 31         # calibration copy for the HBM byte counters
+
+
+def counters_workload(cfg_name):
+    """Workload for rocprofv3 --pmc passes: one plain device copy of
+    COPY_BYTES (calibrates FETCH_SIZE/WRITE_SIZE against known traffic), then
+    one attention call on the workload."""
+    import torch
+    import segment_causal_dit_amd as sc
+    cfg = workloads.CONFIGS[cfg_name]
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    inp = workloads.make_inputs(cfg)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf(inp.q), bf(inp.k), bf(inp.v)
+    cache, hist = None, None
+    if len(cfg.hist_t):
+        cache = sc.KVCache(cfg.n_slots, cfg.n_heads, cfg.tokens_per_frame, cfg.cache_dtype, dev)
+        hk = bf(inp.hist_k)
+        sc.rope3d_apply(hk, torch.from_numpy(inp.hist_pos).to(dev))
+        sc.kv_cache_append(cache, 0, hk, bf(inp.hist_v))
+        cache.slot_t[:] = inp.slot_t
+        hist = torch.from_numpy(sc.window_select(cache.slot_t, cfg.window)).to(dev)
+    torch.cuda.synchronize()
+    sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist)
+    torch.cuda.synchronize()
+    log("counters workload done")
+
+
+def summarize_counters(cfg_name, fetch_dir, write_dir, out_path):
+    """Turn two rocprofv3 --pmc CSV outputs (FETCH_SIZE, WRITE_SIZE) into HBM
+    bytes per attention launch, scaled by the calibration copy."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        copy = [v for (i, n), v in vals.items() if "copy" in n.lower() or "elementwise" in n.lower()]
+        attn = [v for (i, n), v in vals.items() if ATTN_KERNEL in n]
+        return max(copy), attn
+    f_copy, f_attn = read(fetch_dir, "FETCH_SIZE")
+    w_copy, w_attn = read(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / 1024.0 / f_copy      # counters are KiB
+    w_scale = COPY_BYTES / 1024.0 / w_copy
+    fetch = float(np.mean(f_attn)) * 1024.0 * f_scale
+    write = float(np.mean(w_attn)) * 1024.0 * w_scale
+    summary = {
+        "workload": cfg_name, "kernel": ATTN_KERNEL, "attn_source_sha": attn_source_hash(),
+        "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+        "hbm_bytes_per_launch": fetch + write,
+        "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib_read": f_copy,
+                        "write_kib_read": w_copy, "fetch_scale": f_scale, "write_scale": w_scale},
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- "
+            "python3 bench.py --config %s --counters-workload" % cfg_name,
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- "
+            "python3 bench.py --config %s --counters-workload" % cfg_name,
+            "python3 bench.py --config %s --summarize-counters <fetch_dir> <write_dir>" % cfg_name],
+    }
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,7 +166,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c4", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters-workload", action="store_true",
+                    help="one calibration copy + one attention call, for rocprofv3 --pmc")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.config, args.summarize_counters[0], args.summarize_counters[1],
+                           os.path.join(ROOT, "profiles", "attn_%s_counters.json" % args.config))
+        return
+    if args.counters_workload:
+        counters_workload(args.config)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the attention would shard by heads; see the design notes).", file=sys.stderr)
