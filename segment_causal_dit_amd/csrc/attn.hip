@@ -18,29 +18,28 @@
 // Design (one workgroup = 8 waves = 256 query rows of one head, one
 // workgroup per CU, two waves per SIMD):
 //  * each wave owns 32 query rows; Q stays in registers as MFMA B operands;
-//  * waves 0-3 stage the K/V tiles, so each SIMD hosts one staging wave and
-//    one compute-only wave and the staging cost is shared by 256 queries;
-//  * key tiles of 64 rows are staged through LDS, double buffered: K row-major
-//    [key][d] (272-byte rows), V transposed [d][key'] (128-byte rows, 16-byte
-//    chunks XOR-swizzled by row) so that both MFMA operands are single
-//    16-byte LDS reads without bank conflicts;
+//  * key tiles of 64 rows are staged through LDS, double buffered, by direct
+//    global->LDS loads (no staging registers); waves 0-3 stage, so each SIMD
+//    hosts one staging wave and one compute-only wave;
+//  * tiles are row-major with XOR-swizzled 16-byte chunks, chosen for the
+//    gfx950 LDS (16 lanes of a 16-byte read per cycle over 64 banks) so that
+//    every operand read is conflict-free and every load instruction moves 4
+//    whole rows;
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: keys land in accumulator
 //    registers and queries across lanes, so a row max needs only one
 //    cross-half exchange (v_permlane32_swap); O^T = V^T P^T takes the S^T
-//    accumulators as the P operand directly (V^T is stored in the matching
-//    key order);
-//  * software pipeline: the QK^T MFMAs of tile t+1 are issued before the
-//    softmax of tile t, so MFMA and VALU work of one wave overlap; K is
-//    prefetched two tiles ahead and V one tile ahead, with one barrier per tile;
-//  * each wave stages a 16-row group of a tile: with frames of a multiple of
-//    16 tokens a group never straddles a frame, so its base address is
-//    wave-uniform and lanes only add 32-bit offsets; rows past the end are
-//    clamped to the last valid row (finite data) and masked;
+//    accumulators as the P operand directly, and its V^T operand comes from
+//    the row-major V tile through the transposing LDS read (ds_read_b64_tr_b16);
+//  * each staging wave loads a 16-row group of a tile: with frames of a
+//    multiple of 16 tokens a group never straddles a frame, so its base
+//    address is wave-uniform and lanes only add 32-bit offsets; rows past the
+//    end are clamped to the last valid row (finite data) and masked;
+//  * INT8 history rows (codes and scales) are direct-loaded into a staging
+//    area and dequantised to bf16(code * scale) into the tile by the wave that
+//    loaded them, so the MFMA path is the same for both cache types;
 //  * online softmax in base 2 with the rescale of O deferred until the running
 //    max grows by more than 2^8 (exact: the final division uses the same
 //    reference max);
-//  * INT8 history rows are dequantised to bf16(code * scale) while they are
-//    written to LDS, so the MFMA path is the same for both cache types;
 //  * masks are per tile: only tiles at a ragged end or with segment structure
 //    evaluate a per-element predicate from a 64-entry key table in LDS; keys
 //    of later segments than the workgroup's last query are never loaded;
@@ -48,37 +47,25 @@
 //    works through contiguous query tiles of the same head, sharing K/V in L2.
 #include "internal.h"
 
-// Tuning switches (compile time): waves per workgroup (4 or 8; waves 0-3
-// stage K/V tiles, any further waves only compute), minimum waves per SIMD the
-// register allocation must allow, and whether QK^T of the next tile is issued
-// ahead of the softmax of the current one.
-#ifndef SEGC_ATTN_NW
-#define SEGC_ATTN_NW 8
-#endif
-#ifndef SEGC_ATTN_WAVES_PER_SIMD
-#define SEGC_ATTN_WAVES_PER_SIMD 2
-#endif
-#ifndef SEGC_ATTN_PIPELINE
-#define SEGC_ATTN_PIPELINE 0
-#endif
-
 namespace segc {
 namespace {
 
 constexpr int D = 128;
 constexpr int BN = 64;                 // keys per tile
-constexpr int NW = SEGC_ATTN_NW;       // waves per workgroup
+constexpr int NSTAGE = 4;              // waves that stage tiles
+constexpr int RW = BN / NSTAGE;        // tile rows staged per wave (a "group")
+constexpr int NW = 8;                  // waves per workgroup: 0-3 stage and compute, 4-7 compute
 constexpr int NT = NW * 64;
-constexpr int NSTAGE = 4;              // waves that stage tiles (16 rows each)
 constexpr int BM = 32 * NW;            // query rows per workgroup
-constexpr int KS = 136;                // LDS K row stride (bf16 elements, 272 B)
-constexpr int K_BYTES = BN * KS * 2;   // 17408
-constexpr int V_BYTES = D * BN * 2;    // 16384: V^T rows of 64 keys
-constexpr int INFO_BYTES = BN * 4;
-constexpr int KBUF0 = 0;
-constexpr int VBUF0 = 2 * K_BYTES;
-constexpr int INFO0 = VBUF0 + 2 * V_BYTES;
-constexpr int LDS_BYTES = INFO0 + 2 * INFO_BYTES;
+constexpr int TILE_BYTES = BN * D * 2;           // one 64 x 128 bf16 tile
+constexpr int INFO_BYTES = BN * 4;               // per-key visibility table
+constexpr int KOFF = 0, VOFF = TILE_BYTES, IOFF = 2 * TILE_BYTES;
+constexpr int BUF_BYTES = 2 * TILE_BYTES + INFO_BYTES;
+constexpr int NBUF = 2;                          // tile t is read while tile t+1 lands
+constexpr int RAW0 = NBUF * BUF_BYTES;           // INT8 staging: codes, then scales
+constexpr int RAW_KC = 0, RAW_VC = BN * D, RAW_S = 2 * BN * D;
+constexpr int RAW_BYTES = 2 * BN * D + NSTAGE * 256;   // codes + one 64-float scale block per wave
+constexpr int LDS_BYTES = RAW0 + RAW_BYTES;
 constexpr float kTau = 8.0f;           // deferred-rescale threshold (log2 units)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -87,6 +74,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -137,24 +127,26 @@ __device__ inline bool tile_masked(const AttnParams& p, const Tile& tl) {
   return tl.nvalid < BN || (!tl.hist && p.needs_mask);
 }
 
-// Where a wave's 16-row group of a tile lives. Uniform fields describe the
-// group's first row; lanes add row offsets (clamped to `lim`).
+// Where a staging wave's group of RW consecutive tile rows lives. Uniform
+// fields describe the group's first row; lanes add row offsets (clamped to
+// `lim`). With frames of a multiple of RW tokens a group never straddles a
+// frame, so one slot lookup serves the whole group.
 struct Group {
   int64_t row0;   // history: cache row index of the group's first row; current: row index
-  int lim;        // largest valid local row (0..15)
-  bool generic;   // history frames not a multiple of 16 tokens: per-lane rows
+  int lim;        // largest valid local row
+  bool generic;   // history frames not a multiple of RW tokens: per-lane rows
   int j;          // first tile row of the group (generic path)
 };
 
 __device__ inline Group group_at(const AttnParams& p, const Tile& tl, int w, int head) {
   Group g;
   const int last = tl.j0 + tl.nvalid - 1;            // last valid row of the tile
-  const int gs = min(tl.j0 + 16 * w, last & ~15);
+  const int gs = min(tl.j0 + RW * w, last & ~(RW - 1));
   g.lim = last - gs;
   g.generic = false;
   g.j = gs;
   if (tl.hist) {
-    if (p.G % 16 == 0) {
+    if (p.G % RW == 0) {
       const int f = gs / p.G;
       const int slot = p.hist_slots[f];
       g.row0 = ((int64_t)slot * p.n_heads + head) * p.G + (gs - f * p.G);
@@ -176,74 +168,69 @@ __device__ inline int64_t hist_row_generic(const AttnParams& p, const Group& g, 
   return ((int64_t)slot * p.n_heads + head) * p.G + (row - f * p.G);
 }
 
-struct KStage { u32x4 d[4]; float s[2]; };
-struct VStage { u32x4 d[4]; float s[4]; };
+// Tile layouts: 64 rows of 256 bytes (row-major, so a direct-load
+// instruction fills 4 whole rows and reads them coalesced), with the 16-byte
+// chunks of each row XOR-swizzled. On gfx950 the LDS serves 16 lanes of a
+// 16-byte read (32 lanes of an 8-byte read) per cycle from 64 four-byte
+// banks; the swizzles make every operand read conflict-free:
+//  * K: chunk c of row r at c ^ (r & 15); an MFMA operand read takes one
+//    chunk of 16 consecutive rows per 16 lanes -> 16 distinct bank groups;
+//  * V: chunk c of row r at c ^ 4 (r & 3); a 32-lane window of the
+//    transposing read takes 4 adjacent chunks of 4 consecutive rows ->
+//    256 distinct bytes.
+__device__ inline int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2)) << 4); }
 
-// ---- K: 4 instructions x (4 rows x 16 chunks of 16 B) = 16 rows per wave
-__device__ inline void load_k(const AttnParams& p, const Tile& tl, int w, int lane, int head,
-                              KStage& st) {
-  const Group g = group_at(p, tl, w, head);
-  if (!tl.hist || !p.hist_int8) {
-    const int ch = lane & 15;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lr = min(4 * r + (lane >> 4), g.lim);
-      const char* src;
-      if (!tl.hist) {
-        const char* base = (const char*)(p.k + g.row0 * p.k_st + head * p.k_sh);
-        src = base + (uint32_t)(lr * (int)p.k_st * 2);
-      } else if (!g.generic) {
-        const char* base = (const char*)p.hk + g.row0 * 256;
-        src = base + (uint32_t)(lr * 256);
-      } else {
-        src = (const char*)p.hk + hist_row_generic(p, g, lr, head) * 256;
-      }
-      st.d[r] = *(const u32x4*)(src + ch * 16);
-    }
-  } else {
-    const int c16 = lane & 7;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int lr = min(8 * i + (lane >> 3), g.lim);
-      const int64_t row = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
-      st.d[i] = *(const u32x4*)((const char*)p.hk + row * 128 + c16 * 16);
-      st.s[i] = p.hks[row];
-    }
-  }
+// Direct global -> LDS copies: lane l's bytes land at lds_base + size * l
+// (lds_base is wave-uniform).
+__device__ inline void dload16(const void* g, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds_base, 16, 0, 0);
+}
+__device__ inline void dload4(const void* g, char* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds_base, 4, 0, 0);
 }
 
-// ---- V: lane holds 4 consecutive rows (quad) x 8 elements (chunk c8)
-__device__ inline void load_v(const AttnParams& p, const Tile& tl, int w, int lane, int head,
-                              VStage& st) {
+// Issue the loads of staging wave w's group of tile tl: bf16 rows go
+// straight into the K/V tiles of `buf`; INT8 history rows go into `raw`
+// (codes, plus the group's K and V scales) for stage_finish to convert.
+__device__ inline void stage_issue(const AttnParams& p, const Tile& tl, int w, int lane, int head,
+                                   char* buf, char* raw) {
   const Group g = group_at(p, tl, w, head);
-  const int q4 = 4 * (lane >> 4);
-  const int c8 = lane & 15;
   if (!tl.hist || !p.hist_int8) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lr = min(q4 + r, g.lim);
-      const char* src;
+    for (int e = 0; e < RW / 4; ++e) {                     // 4 whole rows per instruction
+      const int row = RW * w + 4 * e + (lane >> 4);        // tile row of this lane's slot
+      const int lr = min(4 * e + (lane >> 4), g.lim);      // group-local row (clamped)
+      const int pc = lane & 15;                            // physical chunk in the LDS row
+      const char *krow, *vrow;
       if (!tl.hist) {
-        const char* base = (const char*)(p.v + g.row0 * p.v_st + head * p.v_sh);
-        src = base + (uint32_t)(lr * (int)p.v_st * 2);
+        krow = (const char*)(p.k + g.row0 * p.k_st + head * p.k_sh) + (uint32_t)(lr * (int)p.k_st * 2);
+        vrow = (const char*)(p.v + g.row0 * p.v_st + head * p.v_sh) + (uint32_t)(lr * (int)p.v_st * 2);
       } else if (!g.generic) {
-        const char* base = (const char*)p.hv + g.row0 * 256;
-        src = base + (uint32_t)(lr * 256);
+        krow = (const char*)p.hk + g.row0 * 256 + (uint32_t)(lr * 256);
+        vrow = (const char*)p.hv + g.row0 * 256 + (uint32_t)(lr * 256);
       } else {
-        src = (const char*)p.hv + hist_row_generic(p, g, lr, head) * 256;
+        const int64_t cr = hist_row_generic(p, g, lr, head);
+        krow = (const char*)p.hk + cr * 256;
+        vrow = (const char*)p.hv + cr * 256;
       }
-      st.d[r] = *(const u32x4*)(src + c8 * 16);
+      char* dst = buf + (RW * w + 4 * e) * 256;
+      dload16(krow + ((pc ^ (row & 15)) << 4), dst + KOFF);
+      dload16(vrow + ((pc ^ ((row & 3) << 2)) << 4), dst + VOFF);
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lr = min(q4 + r, g.lim);
-      const int64_t row = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
-      const u32x2 w2 = *(const u32x2*)((const char*)p.hv + row * 128 + c8 * 8);
-      st.d[r].x = w2.x;
-      st.d[r].y = w2.y;
-      st.s[r] = p.hvs[row];
+    for (int e = 0; e < RW / 8; ++e) {                     // 8 rows of codes per instruction
+      const int lr = min(8 * e + (lane >> 3), g.lim);
+      const int64_t cr = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
+      const int off = (lane & 7) * 16;
+      dload16((const char*)p.hk + cr * 128 + off, raw + RAW_KC + (RW * w + 8 * e) * 128);
+      dload16((const char*)p.hv + cr * 128 + off, raw + RAW_VC + (RW * w + 8 * e) * 128);
     }
+    // scales: lanes [0, RW) K of the group's rows, [RW, 2 RW) V, the rest repeat
+    const int lr = min(lane & (RW - 1), g.lim);
+    const int64_t cr = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
+    dload4((lane & RW) ? (const void*)(p.hvs + cr) : (const void*)(p.hks + cr), raw + RAW_S + w * 256);
   }
 }
 
@@ -257,77 +244,26 @@ __device__ inline void dequant4(uint32_t w, float s, float* out) {
   out[3] = fmaf((float)(u >> 24), s, ms);
 }
 
-__device__ inline void store_k(const AttnParams& p, const Tile& tl, int w, int lane,
-                               const KStage& st, char* kbuf) {
-  if (!tl.hist || !p.hist_int8) {
+template <bool IS_V>
+__device__ inline void convert_group(const char* codes, const float* scales, char* tile, int w,
+                                     int lane) {
+  const int row = RW * w + (lane >> 2), q = lane & 3;
+  const float sc = scales[lane >> 2];
+  const u32x4 c0 = *(const u32x4*)(codes + row * 128 + 32 * q);
+  const u32x4 c1 = *(const u32x4*)(codes + row * 128 + 32 * q + 16);
+  float f[32];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * r + (lane >> 4);
-      *(u32x4*)(kbuf + row * (KS * 2) + (lane & 15) * 16) = st.d[r];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 16 * w + 8 * i + (lane >> 3);
-      float f[16];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dequant4(st.d[i][e], st.s[i], f + 4 * e);
-      u32x4 a, b;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = pack_bf16(f[2 * e], f[2 * e + 1]);
-        b[e] = pack_bf16(f[8 + 2 * e], f[9 + 2 * e]);
-      }
-      char* dst = kbuf + row * (KS * 2) + (lane & 7) * 32;
-      *(u32x4*)dst = a;
-      *(u32x4*)(dst + 16) = b;
-    }
+  for (int e = 0; e < 4; ++e) {
+    dequant4(c0[e], sc, f + 4 * e);
+    dequant4(c1[e], sc, f + 16 + 4 * e);
   }
-}
-
-// V^T byte offset of (row d, keys pos..pos+3) with pos a multiple of 4. Keys
-// are stored with bits 2 and 3 of their index inside each 16-key chunk
-// swapped (pos), and the row's 16-byte chunks XOR-swizzled by (d ^ d>>3) & 7.
-__device__ inline int vt_off(int d, int pos) {
-  const int sw = (d ^ (d >> 3)) & 7;
-  return d * (BN * 2) + ((((pos >> 3) ^ sw) << 4) | ((pos & 4) << 1));
-}
-
-// Position of the 4 keys 4*quad..4*quad+3 inside a V^T row.
-__device__ inline int vt_pos(int quad) {
-  const int m = quad & 3;
-  return (quad >> 2) * 16 + (((m & 1) << 1) | (m >> 1)) * 4;
-}
-
-__device__ inline void store_v(const AttnParams& p, const Tile& tl, int w, int lane,
-                               const VStage& st, char* vbuf) {
-  const int quad = 4 * w + (lane >> 4);
-  const int c8 = lane & 15;
-  const int pos = vt_pos(quad);
-  if (!tl.hist || !p.hist_int8) {
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int e = dd >> 1;
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      u32x2 o2;
-      o2.x = __builtin_amdgcn_perm(st.d[1][e], st.d[0][e], sel);
-      o2.y = __builtin_amdgcn_perm(st.d[3][e], st.d[2][e], sel);
-      *(u32x2*)(vbuf + vt_off(8 * c8 + dd, pos)) = o2;
-    }
-  } else {
-    float f[4][8];
+  for (int e = 0; e < 4; ++e) {
+    u32x4 o;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dequant4(st.d[r].x, st.s[r], f[r]);
-      dequant4(st.d[r].y, st.s[r], f[r] + 4);
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      u32x2 o2;
-      o2.x = pack_bf16(f[0][dd], f[1][dd]);
-      o2.y = pack_bf16(f[2][dd], f[3][dd]);
-      *(u32x2*)(vbuf + vt_off(8 * c8 + dd, pos)) = o2;
-    }
+    for (int k = 0; k < 4; ++k) o[k] = pack_bf16(f[8 * e + 2 * k], f[8 * e + 2 * k + 1]);
+    const int cc = 4 * q + e;
+    *(u32x4*)(tile + (IS_V ? v_off(row, cc) : k_off(row, cc))) = o;
   }
 }
 
@@ -361,12 +297,12 @@ __device__ inline void qk_tile(const char* kbuf, const bf16x8 (&qf)[8], int lr, 
                                f32x16 (&s)[2]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const char* row = kbuf + (32 * kb + lr) * (KS * 2) + hh * 16;
-    bf16x8 a = *(const bf16x8*)row;
+    const int r = 32 * kb + lr;
+    bf16x8 a = *(const bf16x8*)(kbuf + k_off(r, hh));
     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int dt = 1; dt < 8; ++dt) {
-      a = *(const bf16x8*)(row + dt * 32);
+      a = *(const bf16x8*)(kbuf + k_off(r, 2 * dt + hh));
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dt], s[kb], 0, 0, 0);
     }
   }
@@ -417,30 +353,59 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info
 }
 
 // O^T += V^T P^T for one tile; the row sum l accumulates the fp32 P values.
-__device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lr, int hh,
+// The V^T operand comes from the row-major V tile through the transposing
+// LDS read: inside each 16-lane group, lane j addresses 4 elements of row
+// base + j/4 at column d0 + 4 (j % 4); lane i then receives rows base..base+3
+// at column d0 + i, i.e. 4 keys of its own d. Two reads give the 8 keys the
+// P operand holds in this lane half (rows 16 ck + 4 hh + 0..3 and + 8..11).
+__device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane, int hh,
                                f32x16 (&o)[4], RowState& rs) {
+  // lane i of 16-lane group g reads row 16 ck + 4 hh + i / 4 and the row 8
+  // further down, column 32 db + 16 (g & 1) + 4 (i % 4): chunk 4 db + hb with
+  // hb = 2 (g & 1) + (i % 4) / 2, byte 8 (i & 1).
+  const int gi = lane & 15;
+  const int hb = ((gi & 3) >> 1) | (((lane >> 4) & 1) << 1);
+  const int r0 = 4 * hh + (gi >> 2);
+  const int sub = 8 * (gi & 1);
   float ls = 0.0f;
 #pragma unroll
   for (int ck = 0; ck < 4; ++ck) {
     u32x4 u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      u[e] = pack_bf16(s[ck >> 1][8 * (ck & 1) + 2 * e], s[ck >> 1][8 * (ck & 1) + 2 * e + 1]);
-      ls += s[ck >> 1][8 * (ck & 1) + 2 * e] + s[ck >> 1][8 * (ck & 1) + 2 * e + 1];
+      const float x0 = s[ck >> 1][8 * (ck & 1) + 2 * e], x1 = s[ck >> 1][8 * (ck & 1) + 2 * e + 1];
+      u[e] = pack_bf16(x0, x1);
+      ls += x0 + x1;
     }
     const bf16x8 pb = as_bf16x8(u);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + lr;
-      const int sw = (d ^ (d >> 3)) & 7;
-      const bf16x8 a = *(const bf16x8*)(vbuf + d * (BN * 2) + (((2 * ck + hh) ^ sw) << 4));
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vbuf + v_off(16 * ck + r0, 4 * db + hb) + sub));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vbuf + v_off(16 * ck + r0 + 8, 4 * db + hb) + sub));
+      const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb, o[db], 0, 0, 0);
     }
   }
   rs.l += ls;
 }
 
-__global__ __launch_bounds__(NT, SEGC_ATTN_WAVES_PER_SIMD) void attn_kernel(AttnParams p) {
+// Finish staging wave w's group of tile tl: wait for its direct loads, turn
+// INT8 rows into bf16 (each wave converts exactly the rows it loaded), and
+// (wave 0) write the tile's key table when the tile needs a mask.
+__device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, int lane, int tid,
+                                    char* buf, const char* raw) {
+  __builtin_amdgcn_s_waitcnt(0);
+  if (tl.hist && p.hist_int8) {
+    const float* sk = (const float*)(raw + RAW_S + w * 256);   // K scales of the group's rows
+    convert_group<false>(raw + RAW_KC, sk, buf + KOFF, w, lane);
+    convert_group<true>(raw + RAW_VC, sk + RW, buf + VOFF, w, lane);
+  }
+  if (tile_masked(p, tl)) store_info(p, tl, tid, (int*)(buf + IOFF));
+}
+
+__global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -482,101 +447,32 @@ __global__ __launch_bounds__(NT, SEGC_ATTN_WAVES_PER_SIMD) void attn_kernel(Attn
   RowState rs = {-INFINITY, 0.0f};
   const float c = p.scale_log2;
 
+  // Lockstep schedule: every wave computes tile t from LDS buffer t & 1
+  // while the staging waves' direct loads fill buffer (t + 1) & 1 (vacated by
+  // tile t - 1 at the previous barrier); one barrier per tile.
   const bool stager = w < NSTAGE;
-#if SEGC_ATTN_PIPELINE
-  // prologue: K(0), V(0) (+ key table), K(1) into LDS
+  char* const raw = smem + RAW0;
   if (stager) {
-    KStage ks;
-    VStage vs;
     const Tile t0 = tile_at(p, 0, cur_end);
-    load_k(p, t0, w, lane, head, ks);
-    load_v(p, t0, w, lane, head, vs);
-    store_k(p, t0, w, lane, ks, smem + KBUF0);
-    store_v(p, t0, w, lane, vs, smem + VBUF0);
-    if (tile_masked(p, t0)) store_info(p, t0, tid, (int*)(smem + INFO0));
-    if (n_tiles > 1) {
-      const Tile t1 = tile_at(p, 1, cur_end);
-      load_k(p, t1, w, lane, head, ks);
-      store_k(p, t1, w, lane, ks, smem + KBUF0 + K_BYTES);
-    }
+    stage_issue(p, t0, w, lane, head, smem, raw);
+    stage_finish(p, t0, w, lane, tid, smem, raw);
   }
   __syncthreads();
-
-  f32x16 sa[2], sb[2];
-  qk_tile(smem + KBUF0, qf, lr, hh, sa);
-
-  // one pipelined tile: S(t+1) into s_next while s_cur (tile t) is consumed
-  auto step = [&](int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
-    const bool has_v1 = t + 1 < n_tiles;
-    const bool has_k2 = t + 2 < n_tiles;
-    const Tile tt = tile_at(p, t, cur_end);
-    KStage ks;
-    VStage vs;
-    const Tile tk = tile_at(p, t + 2, cur_end);
-    const Tile tv = tile_at(p, t + 1, cur_end);
-    if (has_k2 && stager) load_k(p, tk, w, lane, head, ks);
-    if (has_v1) {
-      if (stager) load_v(p, tv, w, lane, head, vs);
-      qk_tile(smem + KBUF0 + ((t + 1) & 1) * K_BYTES, qf, lr, hh, s_next);
-    }
-    softmax_tile(s_cur, tile_masked(p, tt), (const int*)(smem + INFO0 + (t & 1) * INFO_BYTES), qseg,
-                 hh, c, rs, o);
-    pv_tile(smem + VBUF0 + (t & 1) * V_BYTES, s_cur, lr, hh, o, rs);
-    if (stager) {
-      if (has_k2) store_k(p, tk, w, lane, ks, smem + KBUF0 + (t & 1) * K_BYTES);
-      if (has_v1) {
-        store_v(p, tv, w, lane, vs, smem + VBUF0 + ((t + 1) & 1) * V_BYTES);
-        if (tile_masked(p, tv))
-          store_info(p, tv, tid, (int*)(smem + INFO0 + ((t + 1) & 1) * INFO_BYTES));
-      }
-    }
-    __syncthreads();
-  };
-
-  int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
-  }
-  if (t < n_tiles) step(t, sa, sb);
-#else
-  // prologue: tile 0 into LDS buffer 0
-  if (stager) {
-    KStage ks;
-    VStage vs;
-    const Tile t0 = tile_at(p, 0, cur_end);
-    load_k(p, t0, w, lane, head, ks);
-    load_v(p, t0, w, lane, head, vs);
-    store_k(p, t0, w, lane, ks, smem + KBUF0);
-    store_v(p, t0, w, lane, vs, smem + VBUF0);
-    if (tile_masked(p, t0)) store_info(p, t0, tid, (int*)(smem + INFO0));
-  }
-  __syncthreads();
-
   for (int t = 0; t < n_tiles; ++t) {
     const bool has_next = t + 1 < n_tiles;
-    const Tile tt = tile_at(p, t, cur_end);
+    char* const cur = smem + (t & 1) * BUF_BYTES;
+    char* const next = smem + ((t + 1) & 1) * BUF_BYTES;
     const Tile tn = tile_at(p, t + 1, cur_end);
-    KStage ks;
-    VStage vs;
-    if (has_next && stager) {
-      load_k(p, tn, w, lane, head, ks);
-      load_v(p, tn, w, lane, head, vs);
-    }
-    const int b = t & 1;
+    const bool mt = tile_masked(p, tile_at(p, t, cur_end));
+    const int* info = (const int*)(cur + IOFF);
+    if (stager && has_next) stage_issue(p, tn, w, lane, head, next, raw);
     f32x16 sc[2];
-    qk_tile(smem + KBUF0 + b * K_BYTES, qf, lr, hh, sc);
-    softmax_tile(sc, tile_masked(p, tt), (const int*)(smem + INFO0 + b * INFO_BYTES), qseg, hh, c,
-                 rs, o);
-    pv_tile(smem + VBUF0 + b * V_BYTES, sc, lr, hh, o, rs);
-    if (has_next && stager) {
-      store_k(p, tn, w, lane, ks, smem + KBUF0 + (b ^ 1) * K_BYTES);
-      store_v(p, tn, w, lane, vs, smem + VBUF0 + (b ^ 1) * V_BYTES);
-      if (tile_masked(p, tn)) store_info(p, tn, tid, (int*)(smem + INFO0 + (b ^ 1) * INFO_BYTES));
-    }
+    qk_tile(cur + KOFF, qf, lr, hh, sc);
+    softmax_tile(sc, mt, info, qseg, hh, c, rs, o);
+    pv_tile(cur + VOFF, sc, lane, hh, o, rs);
+    if (stager && has_next) stage_finish(p, tn, w, lane, tid, next, raw);
     __syncthreads();
   }
-#endif
 
   // epilogue: O = acc / l, bf16; lse = m * sm_scale + ln l
   const float lt = xhalf_sum(rs.l);
