@@ -20,7 +20,12 @@
 //  * each wave owns 32 query rows; Q stays in registers as MFMA B operands;
 //  * key tiles of 64 rows are staged through LDS, double buffered, by direct
 //    global->LDS loads (no staging registers); waves 0-3 stage, so each SIMD
-//    hosts one staging wave and one compute-only wave;
+//    hosts one staging wave and one compute-only wave; the loads are issued
+//    from inline assembly and awaited explicitly once per tile, because the
+//    compiler, unable to tell the two LDS buffers apart, would otherwise
+//    drain them before every operand read of the other buffer; all slot
+//    lookups precede the loads of a tile (a wait for a lookup would drain
+//    them too);
 //  * tiles are row-major with XOR-swizzled 16-byte chunks, chosen for the
 //    gfx950 LDS (16 lanes of a 16-byte read per cycle over 64 banks) so that
 //    every operand read is conflict-free and every load instruction moves 4
@@ -131,6 +136,12 @@ __device__ inline bool tile_masked(const AttnParams& p, const Tile& tl) {
 // fields describe the group's first row; lanes add row offsets (clamped to
 // `lim`). With frames of a multiple of RW tokens a group never straddles a
 // frame, so one slot lookup serves the whole group.
+// The slot list is not written while the kernel runs: reading it through the
+// constant address space lets a wave-uniform lookup be a scalar load.
+__device__ inline int const_load(const int* p) {
+  return *(const __attribute__((address_space(4))) int*)p;
+}
+
 struct Group {
   int64_t row0;   // history: cache row index of the group's first row; current: row index
   int lim;        // largest valid local row
@@ -148,7 +159,7 @@ __device__ inline Group group_at(const AttnParams& p, const Tile& tl, int w, int
   if (tl.hist) {
     if (p.G % RW == 0) {
       const int f = gs / p.G;
-      const int slot = p.hist_slots[f];
+      const int slot = const_load(p.hist_slots + f);
       g.row0 = ((int64_t)slot * p.n_heads + head) * p.G + (gs - f * p.G);
     } else {
       g.generic = true;
@@ -183,11 +194,31 @@ __device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2
 
 // Direct global -> LDS copies: lane l's bytes land at lds_base + size * l
 // (lds_base is wave-uniform).
-__device__ inline void dload16(const void* g, char* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds_base, 16, 0, 0);
+// Issued from inline assembly: the compiler then records no pending LDS
+// write, so it does not drain these loads (s_waitcnt vmcnt(0)) before every
+// later LDS read of the other buffer. Completion is awaited explicitly
+// (stage_finish) before the barrier that publishes the tile. M0 holds the
+// LDS base; gfx9 needs one wait state between an SALU write of M0 and an
+// LDS-DMA load. Nothing else in this kernel keeps a value in M0.
+__device__ inline uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
 }
-__device__ inline void dload4(const void* g, char* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds_base, 4, 0, 0);
+__device__ inline void dload16(const void* g, const char* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
+}
+__device__ inline void dload4(const void* g, const char* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
+}
+// A kernel-argument pointer as a wave-uniform value (keeps a per-lane choice
+// between two such pointers a register select, not a per-lane load).
+__device__ inline uintptr_t uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  // readfirstlane yields int: widen each half as unsigned (no sign extension)
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
 // Issue the loads of staging wave w's group of tile tl: bf16 rows go
@@ -197,40 +228,50 @@ __device__ inline void stage_issue(const AttnParams& p, const Tile& tl, int w, i
                                    char* buf, char* raw) {
   const Group g = group_at(p, tl, w, head);
   if (!tl.hist || !p.hist_int8) {
+    // all addresses first: a per-lane slot lookup (generic path) is an
+    // ordinary load, and waiting for it would also drain earlier direct loads
+    const char *krow[RW / 4], *vrow[RW / 4];
 #pragma unroll
     for (int e = 0; e < RW / 4; ++e) {                     // 4 whole rows per instruction
-      const int row = RW * w + 4 * e + (lane >> 4);        // tile row of this lane's slot
       const int lr = min(4 * e + (lane >> 4), g.lim);      // group-local row (clamped)
-      const int pc = lane & 15;                            // physical chunk in the LDS row
-      const char *krow, *vrow;
       if (!tl.hist) {
-        krow = (const char*)(p.k + g.row0 * p.k_st + head * p.k_sh) + (uint32_t)(lr * (int)p.k_st * 2);
-        vrow = (const char*)(p.v + g.row0 * p.v_st + head * p.v_sh) + (uint32_t)(lr * (int)p.v_st * 2);
+        krow[e] = (const char*)(p.k + g.row0 * p.k_st + head * p.k_sh) + (uint32_t)(lr * (int)p.k_st * 2);
+        vrow[e] = (const char*)(p.v + g.row0 * p.v_st + head * p.v_sh) + (uint32_t)(lr * (int)p.v_st * 2);
       } else if (!g.generic) {
-        krow = (const char*)p.hk + g.row0 * 256 + (uint32_t)(lr * 256);
-        vrow = (const char*)p.hv + g.row0 * 256 + (uint32_t)(lr * 256);
+        krow[e] = (const char*)p.hk + g.row0 * 256 + (uint32_t)(lr * 256);
+        vrow[e] = (const char*)p.hv + g.row0 * 256 + (uint32_t)(lr * 256);
       } else {
         const int64_t cr = hist_row_generic(p, g, lr, head);
-        krow = (const char*)p.hk + cr * 256;
-        vrow = (const char*)p.hv + cr * 256;
+        krow[e] = (const char*)p.hk + cr * 256;
+        vrow[e] = (const char*)p.hv + cr * 256;
       }
+    }
+#pragma unroll
+    for (int e = 0; e < RW / 4; ++e) {
+      const int row = RW * w + 4 * e + (lane >> 4);        // tile row of this lane's slot
+      const int pc = lane & 15;                            // physical chunk in the LDS row
       char* dst = buf + (RW * w + 4 * e) * 256;
-      dload16(krow + ((pc ^ (row & 15)) << 4), dst + KOFF);
-      dload16(vrow + ((pc ^ ((row & 3) << 2)) << 4), dst + VOFF);
+      dload16(krow[e] + ((pc ^ (row & 15)) << 4), dst + KOFF);
+      dload16(vrow[e] + ((pc ^ ((row & 3) << 2)) << 4), dst + VOFF);
     }
   } else {
+    int64_t cr[RW / 8];
 #pragma unroll
-    for (int e = 0; e < RW / 8; ++e) {                     // 8 rows of codes per instruction
+    for (int e = 0; e < RW / 8; ++e) {
       const int lr = min(8 * e + (lane >> 3), g.lim);
-      const int64_t cr = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
-      const int off = (lane & 7) * 16;
-      dload16((const char*)p.hk + cr * 128 + off, raw + RAW_KC + (RW * w + 8 * e) * 128);
-      dload16((const char*)p.hv + cr * 128 + off, raw + RAW_VC + (RW * w + 8 * e) * 128);
+      cr[e] = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
     }
     // scales: lanes [0, RW) K of the group's rows, [RW, 2 RW) V, the rest repeat
-    const int lr = min(lane & (RW - 1), g.lim);
-    const int64_t cr = g.generic ? hist_row_generic(p, g, lr, head) : g.row0 + lr;
-    dload4((lane & RW) ? (const void*)(p.hvs + cr) : (const void*)(p.hks + cr), raw + RAW_S + w * 256);
+    const int slr = min(lane & (RW - 1), g.lim);
+    const int64_t scr = g.generic ? hist_row_generic(p, g, slr, head) : g.row0 + slr;
+    const uintptr_t sbase = (lane & RW) ? uniform_ptr(p.hvs) : uniform_ptr(p.hks);
+#pragma unroll
+    for (int e = 0; e < RW / 8; ++e) {                     // 8 rows of codes per instruction
+      const int off = (lane & 7) * 16;
+      dload16((const char*)p.hk + cr[e] * 128 + off, raw + RAW_KC + (RW * w + 8 * e) * 128);
+      dload16((const char*)p.hv + cr[e] * 128 + off, raw + RAW_VC + (RW * w + 8 * e) * 128);
+    }
+    dload4((const void*)(sbase + (uintptr_t)scr * 4), raw + RAW_S + w * 256);
   }
 }
 
@@ -396,7 +437,9 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
 // (wave 0) write the tile's key table when the tile needs a mask.
 __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, int lane, int tid,
                                     char* buf, const char* raw) {
-  __builtin_amdgcn_s_waitcnt(0);
+  // the direct loads are invisible to the compiler: wait in asm with a memory
+  // clobber so that no read of the landed data is scheduled above the wait
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tl.hist && p.hist_int8) {
     const float* sk = (const float*)(raw + RAW_S + w * 256);   // K scales of the group's rows
     convert_group<false>(raw + RAW_KC, sk, buf + KOFF, w, lane);
@@ -440,6 +483,9 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
       qf[t] = as_bf16x8(u);
     }
   }
+  // Settle the Q loads here: a wait for them left inside the loop would also
+  // drain the direct loads in flight there.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16 o[4];
 #pragma unroll
