@@ -378,7 +378,9 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info
   const float mnew = fmaxf(rs.m, mx);
   const bool need = (mnew - rs.m) * c > kTau;          // false for -inf/-inf (NaN)
   if (__builtin_amdgcn_ballot_w64(need)) {
-    const float alpha = __builtin_amdgcn_exp2f((rs.m - mnew) * c);
+    // a row that has seen no visible key yet keeps m = -inf: its factor is 1
+    // (exp2 of -inf - -inf would be NaN and poison O and l for good)
+    const float alpha = (mnew == rs.m) ? 1.0f : __builtin_amdgcn_exp2f((rs.m - mnew) * c);
     rs.m = mnew;
     rs.l *= alpha;
 #pragma unroll

@@ -244,6 +244,25 @@ def test_edge_shapes():
     sc.segcausal_joint_attn(z, z, z, [(0, 0, 0)], 1.0)
 
 
+def test_rows_without_visible_keys_in_early_tiles():
+    # Segment 0 opens with 80 text rows, so the first key tile is invisible to
+    # every query of segment 1 while segment-0 rows of the same wave see it:
+    # the running max of those segment-1 rows is still -inf when the wave
+    # rescales (query rows 96-127 share a wave: 96-103 in segment 0).
+    segs = [(0, 80, 80), (104, 16, 16)]
+    n_cur = 144
+    qb = workloads.normal_bf16(21, (n_cur, 2, HEAD_DIM), 0.1)
+    kb = workloads.normal_bf16(22, (n_cur, 2, HEAD_DIM))
+    vb = workloads.normal_bf16(23, (n_cur, 2, HEAD_DIM))
+    o = sc.segcausal_joint_attn(_bf(qb), _bf(kb), _bf(vb), segs, 0.088)
+    ref, _ = oracle.joint_attn(*(oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb)),
+                               [oracle.Segment(*s) for s in segs], sm_scale=0.088)
+    got = to_f64(o)
+    assert np.isfinite(got).all()
+    mx, mean = attn_errors(got, ref)
+    assert mx <= MAX_ERR and mean <= MEAN_ERR, (mx, mean)
+
+
 # ----------------------------------------------------- c4 at full size ----
 
 @pytest.mark.timeout(900)
