@@ -18,9 +18,12 @@
 // Design (one workgroup = 8 waves = 256 query rows of one head, one
 // workgroup per CU, two waves per SIMD):
 //  * each wave owns 32 query rows; Q stays in registers as MFMA B operands;
-//  * key tiles of 64 rows are staged through LDS, double buffered, by direct
-//    global->LDS loads (no staging registers); waves 0-3 stage, so each SIMD
-//    hosts one staging wave and one compute-only wave; the loads are issued
+//  * key tiles of 64 rows are staged through LDS by direct global->LDS
+//    loads (no staging registers), two tiles ahead in three tile buffers:
+//    the loads issued while tile t is computed belong to tile t+2 and have a
+//    whole tile's time to land before the waves wait for them; waves 0-3
+//    stage, so each SIMD hosts one staging wave and one compute-only wave;
+//    the loads are issued
 //    from inline assembly and awaited explicitly once per tile, because the
 //    compiler, unable to tell the two LDS buffers apart, would otherwise
 //    drain them before every operand read of the other buffer; all slot
@@ -39,9 +42,9 @@
 //    multiple of 16 tokens a group never straddles a frame, so its base
 //    address is wave-uniform and lanes only add 32-bit offsets; rows past the
 //    end are clamped to the last valid row (finite data) and masked;
-//  * INT8 history rows (codes and scales) are direct-loaded into a staging
-//    area and dequantised to bf16(code * scale) into the tile by the wave that
-//    loaded them, so the MFMA path is the same for both cache types;
+//  * INT8 history rows (codes and scales) are direct-loaded into one of two
+//    staging areas and dequantised to bf16(code * scale) into the tile by the
+//    wave that loaded them, so the MFMA path is the same for both cache types;
 //  * online softmax in base 2 with the rescale of O deferred until the running
 //    max grows by more than 2^8 (exact: the final division uses the same
 //    reference max);
@@ -66,11 +69,11 @@ constexpr int TILE_BYTES = BN * D * 2;           // one 64 x 128 bf16 tile
 constexpr int INFO_BYTES = BN * 4;               // per-key visibility table
 constexpr int KOFF = 0, VOFF = TILE_BYTES, IOFF = 2 * TILE_BYTES;
 constexpr int BUF_BYTES = 2 * TILE_BYTES + INFO_BYTES;
-constexpr int NBUF = 2;                          // tile t is read while tile t+1 lands
-constexpr int RAW0 = NBUF * BUF_BYTES;           // INT8 staging: codes, then scales
+constexpr int NBUF = 3;                          // tiles t, t+1 and t+2 are live at once
+constexpr int RAW0 = NBUF * BUF_BYTES;           // two INT8 staging areas: codes, then scales
 constexpr int RAW_KC = 0, RAW_VC = BN * D, RAW_S = 2 * BN * D;
 constexpr int RAW_BYTES = 2 * BN * D + NSTAGE * 256;   // codes + one 64-float scale block per wave
-constexpr int LDS_BYTES = RAW0 + RAW_BYTES;
+constexpr int LDS_BYTES = RAW0 + 2 * RAW_BYTES;
 constexpr float kTau = 8.0f;           // deferred-rescale threshold (log2 units)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -186,11 +189,14 @@ __device__ inline int64_t hist_row_generic(const AttnParams& p, const Group& g, 
 // banks; the swizzles make every operand read conflict-free:
 //  * K: chunk c of row r at c ^ (r & 15); an MFMA operand read takes one
 //    chunk of 16 consecutive rows per 16 lanes -> 16 distinct bank groups;
-//  * V: chunk c of row r at c ^ 4 (r & 3); a 32-lane window of the
-//    transposing read takes 4 adjacent chunks of 4 consecutive rows ->
-//    256 distinct bytes.
+//  * V: chunk c of row r at c ^ 5 (r & 3); a 32-lane window of the
+//    transposing read takes 4 adjacent chunks (an aligned group of 4) of 4
+//    consecutive rows, which the high term 4 (r & 3) sends to 4 distinct
+//    groups -> 256 distinct bytes; the low term (r & 3) makes the INT8
+//    dequantisation stores conflict-free too (16 lanes store chunks
+//    4 q + e, q = 0..3, of 4 consecutive rows: distinct low bits per row).
 __device__ inline int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
-__device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ ((r & 3) << 2)) << 4); }
+__device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ (5 * (r & 3))) << 4); }
 
 // Direct global -> LDS copies: lane l's bytes land at lds_base + size * l
 // (lds_base is wave-uniform).
@@ -224,8 +230,8 @@ __device__ inline uintptr_t uniform_ptr(const void* p) {
 // Issue the loads of staging wave w's group of tile tl: bf16 rows go
 // straight into the K/V tiles of `buf`; INT8 history rows go into `raw`
 // (codes, plus the group's K and V scales) for stage_finish to convert.
-__device__ inline void stage_issue(const AttnParams& p, const Tile& tl, int w, int lane, int head,
-                                   char* buf, char* raw) {
+__device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, int lane, int head,
+                                  char* buf, char* raw) {
   const Group g = group_at(p, tl, w, head);
   if (!tl.hist || !p.hist_int8) {
     // all addresses first: a per-lane slot lookup (generic path) is an
@@ -252,8 +258,9 @@ __device__ inline void stage_issue(const AttnParams& p, const Tile& tl, int w, i
       const int pc = lane & 15;                            // physical chunk in the LDS row
       char* dst = buf + (RW * w + 4 * e) * 256;
       dload16(krow[e] + ((pc ^ (row & 15)) << 4), dst + KOFF);
-      dload16(vrow[e] + ((pc ^ ((row & 3) << 2)) << 4), dst + VOFF);
+      dload16(vrow[e] + ((pc ^ (5 * (row & 3))) << 4), dst + VOFF);
     }
+    return 2 * (RW / 4);
   } else {
     int64_t cr[RW / 8];
 #pragma unroll
@@ -272,6 +279,7 @@ __device__ inline void stage_issue(const AttnParams& p, const Tile& tl, int w, i
       dload16((const char*)p.hv + cr[e] * 128 + off, raw + RAW_VC + (RW * w + 8 * e) * 128);
     }
     dload4((const void*)(sbase + (uintptr_t)scr * 4), raw + RAW_S + w * 256);
+    return 2 * (RW / 8) + 1;
   }
 }
 
@@ -438,10 +446,17 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
 // INT8 rows into bf16 (each wave converts exactly the rows it loaded), and
 // (wave 0) write the tile's key table when the tile needs a mask.
 __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, int lane, int tid,
-                                    char* buf, const char* raw) {
+                                    char* buf, const char* raw, int newer) {
   // the direct loads are invisible to the compiler: wait in asm with a memory
-  // clobber so that no read of the landed data is scheduled above the wait
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // clobber so that no read of the landed data is scheduled above the wait.
+  // Loads complete in order: leaving the `newer` most recent ones (the next
+  // tile's) in flight still waits for every load of this tile.
+  if (newer == 2 * (RW / 4))
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (RW / 4)) : "memory");
+  else if (newer == 2 * (RW / 8) + 1)
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * (RW / 8) + 1) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tl.hist && p.hist_int8) {
     const float* sk = (const float*)(raw + RAW_S + w * 256);   // K scales of the group's rows
     convert_group<false>(raw + RAW_KC, sk, buf + KOFF, w, lane);
@@ -495,31 +510,39 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   RowState rs = {-INFINITY, 0.0f};
   const float c = p.scale_log2;
 
-  // Lockstep schedule: every wave computes tile t from LDS buffer t & 1
-  // while the staging waves' direct loads fill buffer (t + 1) & 1 (vacated by
-  // tile t - 1 at the previous barrier); one barrier per tile.
+  // Lockstep schedule, one barrier per tile, loads two tiles ahead: during
+  // iteration t every wave computes tile t from LDS buffer t % 3 while the
+  // staging waves' direct loads for tile t+2 land in buffer (t+2) % 3 (bf16)
+  // or INT8 staging area t & 1; at the end of the iteration they wait for
+  // tile t+1's loads (issued one iteration earlier) and dequantise it.
   const bool stager = w < NSTAGE;
-  char* const raw = smem + RAW0;
+  char* const raw0 = smem + RAW0;
+  char* const raw1 = smem + RAW0 + RAW_BYTES;
   if (stager) {
     const Tile t0 = tile_at(p, 0, cur_end);
-    stage_issue(p, t0, w, lane, head, smem, raw);
-    stage_finish(p, t0, w, lane, tid, smem, raw);
+    stage_issue(p, t0, w, lane, head, smem, raw0);
+    stage_finish(p, t0, w, lane, tid, smem, raw0, 0);
+    if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, raw1);
   }
   __syncthreads();
+  int bc = 0;
   for (int t = 0; t < n_tiles; ++t) {
-    const bool has_next = t + 1 < n_tiles;
-    char* const cur = smem + (t & 1) * BUF_BYTES;
-    char* const next = smem + ((t + 1) & 1) * BUF_BYTES;
-    const Tile tn = tile_at(p, t + 1, cur_end);
+    char* const cur = smem + bc * BUF_BYTES;
+    char* const nx1 = smem + (bc == NBUF - 1 ? 0 : bc + 1) * BUF_BYTES;
+    char* const nx2 = smem + (bc == 0 ? NBUF - 1 : bc - 1) * BUF_BYTES;
     const bool mt = tile_masked(p, tile_at(p, t, cur_end));
     const int* info = (const int*)(cur + IOFF);
-    if (stager && has_next) stage_issue(p, tn, w, lane, head, next, raw);
+    int issued = 0;
+    if (stager && t + 2 < n_tiles)
+      issued = stage_issue(p, tile_at(p, t + 2, cur_end), w, lane, head, nx2, (t & 1) ? raw1 : raw0);
     f32x16 sc[2];
     qk_tile(cur + KOFF, qf, lr, hh, sc);
     softmax_tile(sc, mt, info, qseg, hh, c, rs, o);
     pv_tile(cur + VOFF, sc, lane, hh, o, rs);
-    if (stager && has_next) stage_finish(p, tn, w, lane, tid, next, raw);
+    if (stager && t + 1 < n_tiles)
+      stage_finish(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued);
     __syncthreads();
+    bc = (bc == NBUF - 1) ? 0 : bc + 1;
   }
 
   // epilogue: O = acc / l, bf16; lse = m * sm_scale + ln l
