@@ -10,10 +10,13 @@
 //   code  = clamp(rint(fp32(x / scale)), -127, 127)  ties to even
 // with scale 0 and all-zero codes for an all-zero row.
 //
-// x / scale is first estimated as x * fp32(1/scale). That estimate is within
-// 2^-16 of the exact quotient and the IEEE quotient within 2^-18, so unless
-// the estimate lies within 2^-15 of a half-integer both round to the same
-// integer; otherwise the IEEE division is done. Codes are bit-exact.
+// x / scale + 128 (the biased code before rounding) is first estimated as
+// fma(x, rcp(scale), 128) with the hardware reciprocal (within 1 ulp): the
+// estimate is within 3.4e-5 of the exact value and the IEEE quotient within
+// 2^-18 of x / scale (|x / scale| <= 127), so unless the estimate lies
+// within 2^-14 of a half-integer both round to the same integer; otherwise
+// the IEEE division decides (an all-zero row, rcp 0, gives codes 0). The
+// division runs in a wave-uniform branch, taken by about one wave in eight.
 //
 // Layout: a workgroup of 256 lanes handles 16 consecutive tokens of one head;
 // 16 lanes per (token, head), 8 elements each. HBM-bound: 776 B per
@@ -33,12 +36,13 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ inline int quant_one(float x, float rcp, float scale) {
-  float q = x * rcp;
-  const float fr = q - floorf(q);
-  if (fabsf(fr - 0.5f) <= 0x1p-15f) q = x / scale;   // IEEE quotient decides
-  const int c = (int)rintf(q);
-  return c < -127 ? -127 : (c > 127 ? 127 : c);
+// max over the 16 lanes of a DPP row (quad swaps, then half-row and row mirrors)
+__device__ inline float row16_max(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, true)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x140, 0xF, 0xF, true)));
+  return a;
 }
 
 // Quantise 8 bf16 values held by this lane (one of 16 lanes of a row);
@@ -53,18 +57,36 @@ __device__ inline u32x2 quant_row8(const u32x4 in, float* scale_out) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
+  a = row16_max(a);
   const float scale = a / 127.0f;                    // IEEE fp32 division
   *scale_out = scale;
-  u32x2 out = {0u, 0u};
-  if (scale != 0.0f) {
-    const float rcp = 1.0f / scale;
+  const float rcp = scale != 0.0f ? __builtin_amdgcn_rcpf(scale) : 0.0f;   // all-zero row: codes 0
+  // |x / scale| <= 127 (1 + 2^-24) < 127.5 since scale = fp32(max|x| / 127),
+  // so the biased code rint(x / scale) + 128 lies in [1, 255]. Its estimate
+  // v = fma(x, rcp, 128) (one rounding) is within 3.4e-5 of the exact
+  // x / scale + 128; away from ties (2^-14) the byte conversion's own
+  // round-to-nearest-even of v gives the biased code.
+  float v[8];
+  bool near = false;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t b = (uint32_t)quant_one(x[i], rcp, scale) & 0xFFu;
-      out[i >> 2] |= b << (8 * (i & 3));
-    }
+  for (int i = 0; i < 8; ++i) {
+    v[i] = fmaf(x[i], rcp, 128.0f);
+    near |= fabsf(v[i] - rintf(v[i])) >= 0.5f - 0x1p-14f;
+  }
+  if (__builtin_amdgcn_ballot_w64(near)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (fabsf(v[i] - rintf(v[i])) >= 0.5f - 0x1p-14f) v[i] = rintf(x[i] / scale) + 128.0f;
+  }
+  // biased byte written in place, then XOR 0x80 per byte gives the
+  // two's-complement code
+  u32x2 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t wd = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wd = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * h + j], j, wd);
+    out[h] = wd ^ 0x80808080u;
   }
   return out;
 }
