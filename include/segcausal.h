@@ -131,6 +131,30 @@ int kv_cache_append(const segc_cache* cache, int32_t first_slot, int32_t n_frame
                     void* stream);
 
 /*
+ * kv_window_dequant -- expand selected frames of an INT8 cache into a BF16
+ * cache, in window order: output slot i (0 <= i < n_frames) receives source
+ * slot slots[i], as bf16(fp32(code * scale)) for every element of K and V.
+ * Attention over the window may then read the BF16 cache with hist_slots =
+ * 0, 1, ..., n_frames - 1 and gives bit-identical outputs to reading the INT8
+ * cache with hist_slots = slots: the values are those the attention forms
+ * when it dequantises a tile itself, computed once per window instead of
+ * once per query tile.
+ * Source: model card, section "Single-GPU Low-Memory Inference" (keys and
+ * values stored in INT8, attention in BF16).
+ * cache  : SEGC_INT8 source (read only).
+ * slots  : device int32 [n_frames]; each entry in [0, cache->n_slots)
+ *          (not checked: device memory).
+ * out    : SEGC_BF16 cache with the same n_heads and tokens_per_frame and
+ *          n_slots >= n_frames; caller-owned, written in slots 0..n_frames-1.
+ * Errors: EINVAL on a bad descriptor, a source that is not INT8, an output
+ *   that is not BF16 or differs in heads/tokens per frame, n_frames outside
+ *   [0, out->n_slots], a null or misaligned slots pointer, more than 2^31
+ *   rows. n_frames == 0 is a no-op.
+ */
+int kv_window_dequant(const segc_cache* cache, const int32_t* slots, int32_t n_frames,
+                      const segc_cache* out, void* stream);
+
+/*
  * window_select -- choose the cached frames the attention reads (host only).
  * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
  * (a bounded set of historical latent frames, default budget 18, excluding
@@ -208,7 +232,7 @@ const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 0)
+#define SEGC_ABI_VERSION ((1 << 16) | 1)
 
 #ifdef __cplusplus
 }

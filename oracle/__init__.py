@@ -31,7 +31,7 @@ convention is a reading, not a printed value: its convention is
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
 from .rope import rope3d, rope3d_bf16, rope_frequencies
-from .quant import quantise_int8, dequantise_int8
+from .quant import quantise_int8, dequantise_int8, dequantise_int8_bf16
 from .window import window_select, WindowError
 from .attention import (Segment, visible_mask, history_keys, joint_attn,
                         joint_attn_rows)

@@ -10,7 +10,9 @@ The pages do not give the quantiser; this build's scheme is:
   scale = fp32(absmax / 127), IEEE fp32 division;
 * code = clamp(round_half_even(fp32(x / scale)), -127, 127), IEEE fp32 division;
 * a token-head whose values are all zero gets scale 0 and all-zero codes;
-* dequantised value = code * scale.
+* dequantised value = code * scale; where attention runs in BF16 the value
+  fed to it is bf16(fp32(code * scale)): the exact product rounded to fp32,
+  then to bf16, both round-to-nearest-even (this build's reading).
 
 Emulating fp32 division: both operands are fp32 values, so the float64
 quotient rounded to fp32 equals the IEEE fp32 quotient (float64 carries
@@ -18,6 +20,8 @@ quotient rounded to fp32 equals the IEEE fp32 quotient (float64 carries
 """
 
 import numpy as np
+
+from .bf16 import round_to_bf16
 
 
 def quantise_int8(x):
@@ -42,3 +46,13 @@ def dequantise_int8(codes, scales):
     """code * scale, exact in float64."""
     return (np.asarray(codes, dtype=np.float64)
             * np.asarray(scales, dtype=np.float64)[..., None])
+
+
+def dequantise_int8_bf16(codes, scales):
+    """bf16(fp32(code * scale)) as float64: the BF16 operand attention uses.
+
+    code * scale is exact in float64 (7 + 24 significant bits); astype(float32)
+    rounds it to nearest even, and round_to_bf16 rounds that to bf16.
+    """
+    exact = dequantise_int8(codes, scales)
+    return round_to_bf16(exact.astype(np.float32).astype(np.float64))

@@ -51,15 +51,17 @@ class SegcAttnArgs(ctypes.Structure):
 
 _lib.rope3d_apply.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp, _f64, _i32, _i32, _i32, _vp]
 _lib.kv_cache_append.argtypes = [ctypes.POINTER(SegcCache), _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
+_lib.kv_window_dequant.argtypes = [ctypes.POINTER(SegcCache), _vp, _i32, ctypes.POINTER(SegcCache), _vp]
 _lib.window_select.argtypes = [_pi32, _i32, _i32, _pi32, _pi32]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
 _lib.segcausal_last_error.restype = ctypes.c_char_p
 _lib.segcausal_abi_version.restype = ctypes.c_int
-for _f in ("rope3d_apply", "kv_cache_append", "window_select", "segcausal_joint_attn"):
+for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
+           "segcausal_joint_attn"):
     getattr(_lib, _f).restype = ctypes.c_int
 
-EXPORTS = ("rope3d_apply", "kv_cache_append", "window_select", "segcausal_joint_attn",
-           "segcausal_last_error", "segcausal_abi_version")
+EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
+           "segcausal_joint_attn", "segcausal_last_error", "segcausal_abi_version")
 
 
 class SegcError(RuntimeError):
@@ -158,6 +160,17 @@ def kv_cache_append(cache, first_slot, k, v, t_first=None, stream=None):
         for f in range(n_frames):
             cache.slot_t[(first_slot + f) % cache.n_slots] = t_first + f
     return n_frames
+
+
+def kv_window_dequant(cache, slots, out, stream=None):
+    """Expand INT8 cache slots `slots` (device int32 tensor, window order)
+    into slots 0..len(slots)-1 of the BF16 KVCache `out`; attention over the
+    window then reads `out` with hist_slots = 0, 1, ... ."""
+    if slots.dtype != torch.int32 or slots.dim() != 1 or not slots.is_contiguous():
+        raise ValueError("slots must be a contiguous 1-D int32 tensor")
+    _check(_lib.kv_window_dequant(ctypes.byref(cache.desc), slots.data_ptr(), slots.shape[0],
+                                  ctypes.byref(out.desc), _stream(stream)))
+    return slots.shape[0]
 
 
 def window_select(slot_t, budget):

@@ -139,6 +139,36 @@ int kv_cache_append(const segc_cache* cache, int32_t first_slot, int32_t n_frame
   return hip_status(segc::launch_append(p, (hipStream_t)stream), "kv_cache_append launch");
 }
 
+int kv_window_dequant(const segc_cache* cache, const int32_t* slots, int32_t n_frames,
+                      const segc_cache* out, void* stream) {
+  int rc = check_cache(cache);
+  if (rc) return rc;
+  if (cache->dtype != SEGC_INT8) return fail(SEGC_EINVAL, "source cache must be SEGC_INT8");
+  rc = check_cache(out);
+  if (rc) return rc;
+  if (out->dtype != SEGC_BF16) return fail(SEGC_EINVAL, "output cache must be SEGC_BF16");
+  if (out->n_heads != cache->n_heads || out->tokens_per_frame != cache->tokens_per_frame)
+    return fail(SEGC_EINVAL, "output cache heads/tokens_per_frame differ from the source cache");
+  if (n_frames < 0 || n_frames > out->n_slots)
+    return fail(SEGC_EINVAL, "n_frames %d outside [0, output n_slots=%d]", n_frames, out->n_slots);
+  const int64_t rows_per_frame = (int64_t)cache->n_heads * cache->tokens_per_frame;
+  if (rows_per_frame * n_frames >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "window too large");
+  if (n_frames == 0) return ok();
+  if (!slots) return fail(SEGC_EINVAL, "slots is NULL");
+  if ((uintptr_t)slots & 3u) return fail(SEGC_EINVAL, "slots must be 4-byte aligned");
+  segc::DequantParams p;
+  p.ck = (const int8_t*)cache->k;
+  p.cv = (const int8_t*)cache->v;
+  p.cks = cache->k_scale;
+  p.cvs = cache->v_scale;
+  p.ok = (uint16_t*)out->k;
+  p.ov = (uint16_t*)out->v;
+  p.slots = slots;
+  p.rows_per_frame = (int32_t)rows_per_frame;
+  p.n_rows = (int32_t)(rows_per_frame * n_frames);
+  return hip_status(segc::launch_dequant(p, (hipStream_t)stream), "kv_window_dequant launch");
+}
+
 int window_select(const int32_t* slot_t, int32_t n_slots, int32_t budget, int32_t* out_slots,
                   int32_t* out_n) {
   if (n_slots < 0) return fail(SEGC_EINVAL, "n_slots < 0");

@@ -39,6 +39,20 @@ struct AppendParams {
 };
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
+// -------------------------------------------------- window dequantise ----
+struct DequantParams {
+  const int8_t* ck;                  // INT8 cache codes [n_slots][H][G][128]
+  const int8_t* cv;
+  const float* cks;                  // INT8 cache scales [n_slots][H][G]
+  const float* cvs;
+  uint16_t* ok;                      // BF16 output cache [>= n][H][G][128]
+  uint16_t* ov;
+  const int32_t* slots;              // device [n]: source slot of output frame i
+  int32_t rows_per_frame;            // H * G
+  int32_t n_rows;                    // n * H * G
+};
+hipError_t launch_dequant(const DequantParams& p, hipStream_t s);
+
 // -------------------------------------------------------- attention ----
 constexpr int kMaxSeg = SEGC_MAX_SEG;
 

@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(sc.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.segcausal_abi_version() == (1 << 16)
+    m = re.search(r"#define SEGC_ABI_VERSION \(\(1 << 16\) \| (\d+)\)", open(HEADER).read())
+    assert m and lib.segcausal_abi_version() == (1 << 16) | int(m.group(1))
 
 
 def test_window_select_matches_oracle():
@@ -107,6 +108,41 @@ def test_append_null_cache_and_noop():
     assert _append(n=0, k=None, v=None) == 0
     # a BF16 cache needs no scales
     assert _append(cache=_cache(dtype=sc.SEGC_BF16, k_scale=None, v_scale=None), n=0) == 0
+
+
+# ------------------------------------------------ window dequantise ----
+
+def _bf16_cache(**kw):
+    c = sc.SegcCache(sc.SEGC_BF16, 16, 128, 880, 8, 0, FAKE, FAKE, None, None)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _dequant(src=None, slots=FAKE, n=3, out=None):
+    s = src if src is not None else _cache()
+    o = out if out is not None else _bf16_cache()
+    return lib.kv_window_dequant(ctypes.byref(s), slots, n, ctypes.byref(o), None)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(src=_cache(dtype=sc.SEGC_BF16, k_scale=None, v_scale=None)), 1),   # source not INT8
+    (dict(out=_cache()), 1),                                                 # output not BF16
+    (dict(out=_bf16_cache(n_heads=8)), 1), (dict(out=_bf16_cache(tokens_per_frame=24)), 1),
+    (dict(out=_bf16_cache(head_dim=64)), 2), (dict(src=_cache(k_scale=None)), 1),
+    (dict(out=_bf16_cache(v=FAKE + 8)), 1), (dict(n=9), 1), (dict(n=-1), 1),
+    (dict(slots=None), 1), (dict(slots=FAKE + 2), 1),
+    (dict(out=_bf16_cache(n_slots=200000), src=_cache(n_slots=200000), n=200000), 1),  # > 2^31 rows
+])
+def test_window_dequant_rejects(args, code):
+    assert _dequant(**args) == code
+
+
+def test_window_dequant_null_descriptors_and_noop():
+    o = _bf16_cache()
+    assert lib.kv_window_dequant(None, FAKE, 1, ctypes.byref(o), None) == 1
+    assert lib.kv_window_dequant(ctypes.byref(_cache()), FAKE, 1, None, None) == 1
+    assert _dequant(n=0, slots=None) == 0
 
 
 # -------------------------------------------------------- attention ----

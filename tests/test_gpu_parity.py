@@ -244,6 +244,58 @@ def test_edge_shapes():
     sc.segcausal_joint_attn(z, z, z, [(0, 0, 0)], 1.0)
 
 
+# ------------------------------------------- window dequantisation ----
+
+def _int8_cache_from(codes_k, codes_v, sk, sv):
+    import torch
+    f, h, g, _ = codes_k.shape
+    c = sc.KVCache(f, h, g, "int8")
+    c.k.copy_(torch.from_numpy(codes_k)); c.v.copy_(torch.from_numpy(codes_v))
+    c.k_scale.copy_(torch.from_numpy(sk)); c.v_scale.copy_(torch.from_numpy(sv))
+    return c
+
+
+def _dequant_window(cache, slots):
+    import torch
+    out = sc.KVCache(len(slots), cache.desc.n_heads, cache.tokens_per_frame, "bf16")
+    sc.kv_window_dequant(cache, torch.from_numpy(np.asarray(slots, np.int32)).cuda(), out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("wide_scales", [False, True])
+def test_window_dequant_bit_exact(wide_scales):
+    cfg = workloads.VARIANTS["mid_int8"]
+    kc, vc, ks, vs = workloads.direct_int8_cache(cfg, 7)
+    if wide_scales:   # scales spanning many binades exercise both roundings
+        rng = np.random.default_rng(61)
+        ks = (ks * 2.0 ** rng.integers(-30, 20, ks.shape)).astype(np.float32)
+        vs = (vs * 2.0 ** rng.integers(-30, 20, vs.shape)).astype(np.float32)
+    cache = _int8_cache_from(kc, vc, ks, vs)
+    slots = [5, 0, 3, 6, 1]                       # a permuted, partial window
+    out = _dequant_window(cache, slots)
+    for t, s in enumerate(slots):
+        ek = oracle.f64_to_bf16_bits(oracle.dequantise_int8_bf16(kc[s], ks[s]))
+        ev = oracle.f64_to_bf16_bits(oracle.dequantise_int8_bf16(vc[s], vs[s]))
+        assert np.array_equal(bits(out.k[t]), ek), t
+        assert np.array_equal(bits(out.v[t]), ev), t
+
+
+@pytest.mark.parametrize("name", ["mid_int8", "c3"])
+def test_attention_over_dequantised_window_is_bit_identical(name):
+    import torch
+    inp = workloads.make_inputs(workloads.ALL[name])
+    r = gpu_chain(inp, with_lse=True)
+    win = _dequant_window(r.cache, r.slots)
+    lse = torch.empty_like(r.lse)
+    o = sc.segcausal_joint_attn(r.q, r.k, r.v, inp.segments, inp.cfg.sm_scale, cache=win,
+                                hist_slots=torch.arange(len(r.slots), dtype=torch.int32, device="cuda"),
+                                lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o, r.o)
+    assert torch.equal(lse, r.lse)
+
+
 def test_rows_without_visible_keys_in_early_tiles():
     # Segment 0 opens with 80 text rows, so the first key tile is invisible to
     # every query of segment 1 while segment-0 rows of the same wave see it:
@@ -293,6 +345,14 @@ def test_c4_append_and_rope_bit_exact():
         kc, ks = oracle.quantise_int8(kf.transpose(1, 0, 2))
         assert np.array_equal(r.cache.k[f].cpu().numpy(), kc)
         assert np.array_equal(r.cache.k_scale[f].cpu().numpy(), ks)
+    # the BF16-window form of the same attention is bit-identical
+    import torch
+    win = _dequant_window(r.cache, r.slots)
+    o2 = sc.segcausal_joint_attn(r.q, r.k, r.v, inp.segments, cfg.sm_scale, cache=win,
+                                 hist_slots=torch.arange(len(r.slots), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o2, r.o)
+    del win, o2
     # attention on sampled rows, reading the cache exactly as the oracle builds it
     rows = np.concatenate([np.arange(0, 256, 4), 256 + rng.choice(cfg.n_video, 192, replace=False)])
     _say("c4 oracle rows", len(rows))

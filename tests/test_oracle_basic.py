@@ -228,3 +228,37 @@ def test_workload_geometry_matches_pages():
     assert per_tok * g["dit_layers"]["value"] * c4.tokens_per_frame == \
         g["int8_kv_bytes_per_frame_54_layers"]["value"]
     assert c4.n_hist_rows == 253440 and c4.n_cur == 63616
+
+
+# ---------------------------------------- dequantisation to the BF16 operand ----
+
+def _f32_mul_then_bf16_bits(codes, scales):
+    """Independent path: IEEE fp32 multiply in numpy float32, then bf16
+    round-to-nearest-even done on the integer bit pattern."""
+    prod = codes.astype(np.float32) * scales.astype(np.float32)[..., None]
+    b = prod.view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def test_dequant_bf16_matches_fp32_product_rounded_to_bf16():
+    rng = np.random.default_rng(31)
+    codes = rng.integers(-127, 128, size=(64, 128)).astype(np.int8)
+    scales = (rng.random(64) * 10.0 ** rng.uniform(-6, 2, 64)).astype(np.float32)
+    got = oracle.f64_to_bf16_bits(oracle.dequantise_int8_bf16(codes, scales))
+    assert np.array_equal(got, _f32_mul_then_bf16_bits(codes, scales))
+
+
+def test_dequant_bf16_closed_forms():
+    codes = np.arange(-127, 128, dtype=np.int8)[None, :]
+    # power-of-two scale: the product has <= 7 significant bits, exact in bf16
+    for k in (-20, -3, 0, 5):
+        s = np.array([2.0 ** k], dtype=np.float32)
+        assert np.array_equal(oracle.dequantise_int8_bf16(codes, s), codes.astype(np.float64) * 2.0 ** k)
+    # zero scale -> zeros; sign symmetry; error within the two roundings
+    assert not np.any(oracle.dequantise_int8_bf16(codes, np.zeros(1, np.float32)))
+    s = np.array([0.0123456], dtype=np.float32)
+    d = oracle.dequantise_int8_bf16(codes, s)
+    assert np.array_equal(d, -oracle.dequantise_int8_bf16((-codes.astype(np.int16)).astype(np.int8), s))
+    exact = oracle.dequantise_int8(codes, s)
+    assert np.all(np.abs(d - exact) <= np.abs(exact) * (2.0 ** -8 + 2.0 ** -24))
