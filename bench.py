@@ -42,15 +42,27 @@ def attn_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(cfg_name):
+def history_path(cfg, int8_attn="window"):
+    """How the attention reads the history in this run (the counter summary
+    is only valid for the same path)."""
+    if not len(cfg.hist_t):
+        return "none"
+    if cfg.cache_dtype == "int8":
+        return "int8 window expanded to bf16" if int8_attn == "window" else "int8 cache"
+    return "bf16 cache"
+
+
+def measured_traffic(cfg, path):
     """HBM bytes per attention launch from the committed counter summary, or
-    None when it is missing or was taken on a different kernel source."""
+    None when it is missing or was taken on a different kernel source or
+    history path."""
     try:
-        with open(os.path.join(ROOT, "profiles", "attn_%s_counters.json" % cfg_name)) as f:
+        with open(os.path.join(ROOT, "profiles", "attn_%s_counters.json" % cfg.name)) as f:
             s = json.load(f)
     except (OSError, ValueError):
         return None
-    if s.get("attn_source_sha") != attn_source_hash() or s.get("workload") != cfg_name:
+    if (s.get("attn_source_sha") != attn_source_hash() or s.get("workload") != cfg.name
+            or s.get("history_path") != path):
         return None
     return s.get("hbm_bytes_per_launch")
 
@@ -112,6 +124,10 @@ def counters_workload(cfg_name):
         sc.kv_cache_append(cache, 0, hk, bf(inp.hist_v))
         cache.slot_t[:] = inp.slot_t
         hist = torch.from_numpy(sc.window_select(cache.slot_t, cfg.window)).to(dev)
+        if cfg.cache_dtype == "int8":       # the bench's path: expand the window, attend over bf16
+            win = sc.KVCache(len(hist), cfg.n_heads, cfg.tokens_per_frame, "bf16", dev)
+            sc.kv_window_dequant(cache, hist, win)
+            cache, hist = win, torch.arange(len(hist), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist)
     torch.cuda.synchronize()
@@ -143,6 +159,7 @@ def summarize_counters(cfg_name, fetch_dir, write_dir, out_path):
     write = float(np.mean(w_attn)) * 1024.0 * w_scale
     summary = {
         "workload": cfg_name, "kernel": ATTN_KERNEL, "attn_source_sha": attn_source_hash(),
+        "history_path": history_path(workloads.CONFIGS[cfg_name]),
         "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
         "hbm_bytes_per_launch": fetch + write,
         "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib_read": f_copy,
@@ -166,6 +183,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c4", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--int8-attn", choices=("window", "cache"), default="window",
+                    help="INT8 history: expand the window to bf16 once per layer-step (window) "
+                         "or dequantise inside every attention workgroup (cache)")
     ap.add_argument("--counters-workload", action="store_true",
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -210,10 +230,12 @@ def main():
         sc.kv_cache_append(cache, 0, hk, bf(inp.hist_v))
         cache.slot_t[:] = inp.slot_t
         del hk
+    expand = cache is not None and cfg.cache_dtype == "int8" and args.int8_attn == "window"
+    win = sc.KVCache(min(cfg.window, n_hist_frames), h, g, "bf16", dev) if expand else None
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = {k_: [] for k_ in ("rope", "attn", "append")}
+    ev = {k_: [] for k_ in ("rope", "dequant", "attn", "append")}
 
     def rec(name, fn):
         a = torch.cuda.Event(enable_timing=True)
@@ -226,12 +248,17 @@ def main():
     def one_step():
         slots = sc.window_select(cache.slot_t[:n_hist_frames], cfg.window) if cache else None
         hist = torch.from_numpy(slots).to(dev, non_blocking=False) if cache else None
+        acache, ahist = cache, hist
+        if expand:
+            acache, ahist = win, torch.arange(len(slots), dtype=torch.int32, device=dev)
         for _ in range(DENOISE_STEPS):
             rec("rope", lambda: (sc.rope3d_apply(q_pre[tl:], pos, x_out=q[tl:]),
                                  sc.rope3d_apply(k_pre[tl:], pos, x_out=k[tl:])))
+            if expand:   # once per layer-step: a model's other layers reuse the buffer between steps
+                rec("dequant", lambda: sc.kv_window_dequant(cache, hist, win))
             rec("attn", lambda: sc.segcausal_joint_attn(q, k, v, [(0, tl, seg.text_valid)],
-                                                        cfg.sm_scale, cache=cache,
-                                                        hist_slots=hist, out=out))
+                                                        cfg.sm_scale, cache=acache,
+                                                        hist_slots=ahist, out=out))
         if cache is not None and cfg.append:
             rec("append", lambda: sc.kv_cache_append(cache, n_hist_frames, k[tl:], v[tl:]))
 
@@ -258,6 +285,8 @@ def main():
         return float(np.mean(xs)) if xs else 0.0
 
     attn_ms, rope_ms, app_ms = avg_ms("attn"), avg_ms("rope"), avg_ms("append")
+    deq_ms = avg_ms("dequant")
+    deq_bytes = (cfg.n_hist_rows * h * (HEAD_DIM + 4 + HEAD_DIM * 2) * 2) if expand else 0
     flops = cfg.flops()
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     step_tflops = DENOISE_STEPS * flops / (ms_step * 1e-3) / 1e12
@@ -270,8 +299,10 @@ def main():
         % (attn_ms, attn_tflops, 100 * attn_tflops / PEAK_BF16_TFLOPS, rope_ms,
            rope_bytes / (rope_ms * 1e-3) / 1e9 if rope_ms else 0, app_ms,
            app_bytes / (app_ms * 1e-3) / 1e9 if app_ms else 0, ms_step))
+    if expand:
+        log("window dequant %.3f ms (%.0f GB/s)" % (deq_ms, deq_bytes / (deq_ms * 1e-3) / 1e9))
 
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg, history_path(cfg, args.int8_attn))
     line = {
         "metric": METRIC,
         "value": round(step_tflops, 3),
@@ -288,25 +319,28 @@ def main():
         "config": {
             "workload": "%s: %d current queries (%d text + %d video) x %d heads x 128 over "
                         "%d %s history keys + the current segment; 8 denoising layer-steps "
-                        "(RoPE q,k + attention) + window select + append per step"
-                        % (cfg.name, cfg.n_cur, tl, n_vid, h, cfg.n_hist_rows, cfg.cache_dtype),
+                        "(RoPE q,k + %sattention) + window select + append per step"
+                        % (cfg.name, cfg.n_cur, tl, n_vid, h, cfg.n_hist_rows, cfg.cache_dtype,
+                           "INT8 window expanded to bf16 + " if expand else ""),
             "n_cur": cfg.n_cur, "n_hist_keys": cfg.n_hist_rows, "heads": h,
             "head_dim": HEAD_DIM, "cache": cfg.cache_dtype,
         },
         "video_tokens_per_s_per_layer_step": round(vid_tok_s, 1),
         "kernels_ms": {"attn": round(attn_ms, 4), "rope_qk": round(rope_ms, 4),
-                       "append": round(app_ms, 4)},
+                       "append": round(app_ms, 4), "window_dequant": round(deq_ms, 4) if expand else None},
         "hbm_frac": {"rope_qk": round(rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
                      if rope_ms else None,
                      "append": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-                     if app_ms else None},
+                     if app_ms else None,
+                     "window_dequant": round(deq_bytes / (deq_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                     if expand and deq_ms else None},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
-        del q_pre, k_pre, q, k, v, out, cache
+        del q_pre, k_pre, q, k, v, out, cache, win
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     else:
