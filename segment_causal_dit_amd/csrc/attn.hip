@@ -38,6 +38,8 @@
 //    cross-half exchange (v_permlane32_swap); O^T = V^T P^T takes the S^T
 //    accumulators as the P operand directly, and its V^T operand comes from
 //    the row-major V tile through the transposing LDS read (ds_read_b64_tr_b16);
+//    the QK^T MFMAs run as two interleaved accumulation chains (the two key
+//    blocks) with their operand reads scheduled 4 MFMAs ahead;
 //  * each staging wave loads a 16-row group of a tile: with frames of a
 //    multiple of 16 tokens a group never straddles a frame, so its base
 //    address is wave-uniform and lanes only add 32-bit offsets; rows past the
@@ -341,20 +343,28 @@ __device__ inline void store_info(const AttnParams& p, const Tile& tl, int tid, 
   info[tid] = lo | (hi << 16);
 }
 
-// S^T (64 keys x 32 queries) = K Q^T from the K tile in LDS.
+// S^T (64 keys x 32 queries) = K Q^T from the K tile in LDS: the two key
+// blocks form two independent accumulation chains, interleaved, with the
+// operand reads kept 4 MFMAs ahead of their use.
 __device__ inline void qk_tile(const char* kbuf, const bf16x8 (&qf)[8], int lr, int hh,
                                f32x16 (&s)[2]) {
+  bf16x8 a[16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = 32 * kb + lr;
-    bf16x8 a = *(const bf16x8*)(kbuf + k_off(r, hh));
-    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0], f32x16{}, 0, 0, 0);
+  for (int i = 0; i < 16; ++i) a[i] = *(const bf16x8*)(kbuf + k_off(32 * (i & 1) + lr, 2 * (i >> 1) + hh));
+  s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[0], f32x16{}, 0, 0, 0);
+  s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int dt = 1; dt < 8; ++dt) {
-      a = *(const bf16x8*)(kbuf + k_off(r, 2 * dt + hh));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dt], s[kb], 0, 0, 0);
-    }
+  for (int dt = 1; dt < 8; ++dt) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * dt], qf[dt], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * dt + 1], qf[dt], s[1], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 struct RowState {
