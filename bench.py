@@ -67,7 +67,7 @@ def measured_traffic(cfg, path):
     return s.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, n_rows=1024):
+def cpu_baseline(cfg, inp, n_rows=512):
     """The fp64 oracle's attention on a bounded sample of the workload: all
     heads of n_rows random query rows against every key. History codes are
     drawn directly (seeded), so no GPU result feeds the oracle."""
