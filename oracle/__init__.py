@@ -20,6 +20,8 @@ describing Hy-Nomas:
   an RTX 4090", Step 2 "Segment-wise causal joint attention".
 * "Tencent Opens Hy-Nomas, an Interactive Video World Model Running on One
   RTX 4090", section "How the RTX 4090 configuration saves memory".
+* The Explainer's section "The training recipe" (segment forcing on packed
+  sequences) for the gradients of the packed form (attention_bwd.py).
 
 Readings where the pages leave a step open are listed in each module.
 
@@ -33,6 +35,7 @@ from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
 from .rope import rope3d, rope3d_bf16, rope_frequencies
 from .quant import quantise_int8, dequantise_int8, dequantise_int8_bf16
 from .window import window_select, WindowError
+from .attention_bwd import joint_attn_backward
 from .attention import (Segment, visible_mask, history_keys, joint_attn,
                         joint_attn_rows)
 
