@@ -227,12 +227,72 @@ typedef struct segc_attn_args {
  */
 int segcausal_joint_attn(const segc_attn_args* args, void* stream);
 
+/*
+ * segcausal_joint_attn_bwd -- gradients of segcausal_joint_attn in the packed
+ * training form (every segment of the sequence present, no history).
+ * Source: "Hy-Nomas Explained ...", section "The training recipe" (segment
+ * forcing on sequences packed offline, up to 360,000 tokens), differentiating
+ * the attention and mask of segcausal_joint_attn above.
+ *
+ * With p_ij = exp(sm_scale * q_i . k_j - lse_i) over the keys query i sees
+ * (the same mask as the forward with n_hist = 0) and do = dL/do:
+ *   delta_i = do_i . o_i
+ *   dv_j = sum_i p_ij do_i
+ *   ds_ij = p_ij * (do_i . v_j - delta_i)
+ *   dq_i = sm_scale * sum_j ds_ij k_j,   dk_j = sm_scale * sum_i ds_ij q_i
+ * Computed with bf16 MFMA products and fp32 accumulation; p and ds are rounded
+ * to bf16 as MFMA operands; dq, dk, dv are written as bf16 (overwritten, not
+ * accumulated). Keys no query sees (padded text rows) get dk = dv = 0.
+ */
+typedef struct segc_attn_bwd_args {
+  const void* q;      /* bf16 [n] rows, the forward's q (after RoPE) */
+  const void* k;      /* bf16 [n] rows, the forward's k (after RoPE) */
+  const void* v;      /* bf16 [n] rows */
+  const void* o;      /* bf16 [n] rows, the forward's output */
+  const void* dout;   /* bf16 [n] rows, dL/do */
+  void*       dq;     /* bf16 [n] rows, output */
+  void*       dk;     /* bf16 [n] rows, output */
+  void*       dv;     /* bf16 [n] rows, output */
+  int64_t q_stride_tok, q_stride_head;
+  int64_t k_stride_tok, k_stride_head;
+  int64_t v_stride_tok, v_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t do_stride_tok, do_stride_head;
+  int64_t dq_stride_tok, dq_stride_head;
+  int64_t dk_stride_tok, dk_stride_head;
+  int64_t dv_stride_tok, dv_stride_head;
+  const float* lse;   /* fp32 [n_heads][n], natural log, as the forward wrote it */
+  float* delta;       /* fp32 [n_heads][n], caller-owned workspace, receives delta */
+  int64_t n;
+  int32_t n_heads;
+  int32_t head_dim;                /* must be 128 */
+  int32_t n_seg;                   /* 1 .. SEGC_MAX_SEG */
+  int32_t reserved;
+  const int32_t* seg_start;        /* host [n_seg + 1], as for segcausal_joint_attn */
+  const int32_t* seg_text_len;     /* host [n_seg] */
+  const int32_t* seg_text_valid;   /* host [n_seg] */
+  float   sm_scale;                /* > 0, the forward's */
+} segc_attn_bwd_args;
+
+/*
+ * Errors: EINVAL on null/misaligned pointers (rows 16-byte aligned, lse and
+ *   delta 4-byte aligned), n < 0 or n >= 2^30, bad strides, bad segment
+ *   tables (as for segcausal_joint_attn, including a segment whose queries
+ *   would see no key), sm_scale <= 0 or not finite, an output (dq, dk, dv,
+ *   delta) whose base pointer equals another argument's (in-place);
+ *   EUNSUPPORTED if head_dim != 128 or n_seg outside [1, SEGC_MAX_SEG].
+ *   n == 0 is a no-op. Outputs must not overlap inputs or each other
+ *   element-wise (a precondition beyond the base-pointer check; interleaved
+ *   views of one buffer are fine).
+ */
+int segcausal_joint_attn_bwd(const segc_attn_bwd_args* args, void* stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 1)
+#define SEGC_ABI_VERSION ((1 << 16) | 2)
 
 #ifdef __cplusplus
 }

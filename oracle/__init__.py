@@ -35,7 +35,7 @@ from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, round_to_bf16
 from .rope import rope3d, rope3d_bf16, rope_frequencies
 from .quant import quantise_int8, dequantise_int8, dequantise_int8_bf16
 from .window import window_select, WindowError
-from .attention_bwd import joint_attn_backward
+from .attention_bwd import joint_attn_backward, joint_attn_dq_rows
 from .attention import (Segment, visible_mask, history_keys, joint_attn,
                         joint_attn_rows)
 
@@ -45,4 +45,5 @@ __all__ = [
     "quantise_int8", "dequantise_int8",
     "window_select", "WindowError",
     "Segment", "visible_mask", "history_keys", "joint_attn", "joint_attn_rows",
+    "dequantise_int8_bf16", "joint_attn_backward", "joint_attn_dq_rows",
 ]

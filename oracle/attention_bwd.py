@@ -20,7 +20,9 @@ over visible j):
 
 Pinned by central finite differences of L = sum(do * o) on tiny inputs and by
 the invariants sum_j dv_j = sum_i do_i and dq = 0 when every visible key is the
-same vector (tests/test_oracle_backward.py).
+same vector (tests/test_oracle_backward.py). `joint_attn_dq_rows` (dq of
+selected query rows only, for sequences too long for the full gradient) is
+pinned by finite differences on its own.
 """
 
 import numpy as np
@@ -57,3 +59,28 @@ def joint_attn_backward(q, k, v, segments, do, sm_scale=1.0, chunk=512):
             dk[:, hd] += sm_scale * (ds.T @ qh[a:b])
             dv[:, hd] += p.T @ doh[a:b]
     return dq, dk, dv
+
+
+def joint_attn_dq_rows(q, k, v, segments, do, rows, sm_scale=1.0):
+    """dq of the selected query rows, float64 [len(rows), H, D].
+
+    Row i needs only its own softmax row: p_i over visible keys, o_i = p_i v,
+    D_i = do_i . o_i, ds_i = p_i (v do_i - D_i), dq_i = sm_scale ds_i k.
+    """
+    q, do = np.asarray(q, dtype=np.float64), np.asarray(do, dtype=np.float64)
+    k, v = np.asarray(k, dtype=np.float64), np.asarray(v, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    n, h, d = q.shape
+    mask = visible_mask(0, segments, n, rows=rows)
+    out = np.zeros((len(rows), h, d))
+    for hd in range(h):
+        s = sm_scale * (q[rows, hd] @ k[:, hd].T)
+        s = np.where(mask, s, -np.inf)
+        m = np.max(s, axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / np.sum(e, axis=1, keepdims=True)
+        o = p @ v[:, hd]
+        big_d = np.sum(do[rows, hd] * o, axis=1, keepdims=True)
+        ds = p * (do[rows, hd] @ v[:, hd].T - big_d)
+        out[:, hd] = sm_scale * (ds @ k[:, hd])
+    return out

@@ -49,19 +49,32 @@ class SegcAttnArgs(ctypes.Structure):
                 ("n_hist", _i32), ("sm_scale", _f32)]
 
 
+class SegcAttnBwdArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp), ("dout", _vp),
+                ("dq", _vp), ("dk", _vp), ("dv", _vp)] + \
+               [(nm + suf, _i64) for nm in ("q", "k", "v", "o", "do", "dq", "dk", "dv")
+                for suf in ("_stride_tok", "_stride_head")] + \
+               [("lse", _vp), ("delta", _vp), ("n", _i64), ("n_heads", _i32), ("head_dim", _i32),
+                ("n_seg", _i32), ("reserved", _i32),
+                ("seg_start", _pi32), ("seg_text_len", _pi32), ("seg_text_valid", _pi32),
+                ("sm_scale", _f32)]
+
+
 _lib.rope3d_apply.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp, _f64, _i32, _i32, _i32, _vp]
 _lib.kv_cache_append.argtypes = [ctypes.POINTER(SegcCache), _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
 _lib.kv_window_dequant.argtypes = [ctypes.POINTER(SegcCache), _vp, _i32, ctypes.POINTER(SegcCache), _vp]
 _lib.window_select.argtypes = [_pi32, _i32, _i32, _pi32, _pi32]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
+_lib.segcausal_joint_attn_bwd.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
 _lib.segcausal_last_error.restype = ctypes.c_char_p
 _lib.segcausal_abi_version.restype = ctypes.c_int
 for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn"):
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_last_error", "segcausal_abi_version")
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "segcausal_last_error",
+           "segcausal_abi_version")
 
 
 class SegcError(RuntimeError):
@@ -199,10 +212,7 @@ def segcausal_joint_attn(q, k, v, segments, sm_scale, cache=None, hist_slots=Non
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     po, ost, osh = _rows(out, "out")
     n_cur, nh = q.shape[0], q.shape[1]
-    starts = [int(s[0]) for s in segments] + [n_cur]
-    seg_start = (ctypes.c_int32 * len(starts))(*starts)
-    tl = (ctypes.c_int32 * max(1, len(segments)))(*[int(s[1]) for s in segments])
-    tv = (ctypes.c_int32 * max(1, len(segments)))(*[int(s[2]) for s in segments])
+    seg_start, tl, tv = _segment_tables(segments, n_cur)
     n_hist = 0
     hs_ptr = None
     cache_ptr = None
@@ -222,6 +232,47 @@ def segcausal_joint_attn(q, k, v, segments, sm_scale, cache=None, hist_slots=Non
                         float(sm_scale))
     _check(_lib.segcausal_joint_attn(ctypes.byref(args), _stream(stream)))
     return out
+
+
+def _segment_tables(segments, n):
+    starts = [int(s[0]) for s in segments] + [n]
+    seg_start = (ctypes.c_int32 * len(starts))(*starts)
+    tl = (ctypes.c_int32 * max(1, len(segments)))(*[int(s[1]) for s in segments])
+    tv = (ctypes.c_int32 * max(1, len(segments)))(*[int(s[2]) for s in segments])
+    return seg_start, tl, tv
+
+
+def segcausal_joint_attn_bwd(q, k, v, o, dout, lse, segments, sm_scale, dq=None, dk=None,
+                             dv=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of the packed-form attention (no history).
+
+    q, k, v, o, dout : bf16 [n, H, 128]; lse: fp32 [H, n] from the forward
+    segments         : list of (start, text_len, text_valid)
+    dq, dk, dv       : optional bf16 [n, H, 128] outputs; delta: optional fp32
+                       [H, n] workspace (receives rowsum(dout * o))
+    """
+    n, nh = q.shape[0], q.shape[1]
+    outs = []
+    for t in (dq, dk, dv):
+        outs.append(torch.empty_like(q, memory_format=torch.contiguous_format) if t is None else t)
+    dq, dk, dv = outs
+    if delta is None:
+        delta = torch.empty((nh, n), dtype=torch.float32, device=q.device)
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (nh, n) or not t.is_contiguous():
+            raise ValueError("%s must be contiguous fp32 [H, n]" % name)
+    rows = [_rows(t, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"),
+                                        (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    for t, nm in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if tuple(t.shape[:2]) != (n, nh):
+            raise ValueError("%s must be [%d, %d, 128] like q" % (nm, n, nh))
+    strides = [x for r in rows for x in r[1:]]
+    seg_start, tl, tv = _segment_tables(segments, n)
+    args = SegcAttnBwdArgs(*([r[0] for r in rows] + strides +
+                             [lse.data_ptr(), delta.data_ptr(), n, nh, HEAD_DIM, len(segments), 0,
+                              seg_start, tl, tv, float(sm_scale)]))
+    _check(_lib.segcausal_joint_attn_bwd(ctypes.byref(args), _stream(stream)))
+    return dq, dk, dv
 
 
 def raw_library():

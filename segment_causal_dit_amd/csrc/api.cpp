@@ -38,6 +38,38 @@ bool strides_ok(int64_t st, int64_t sh) {
   return st >= 0 && sh >= 0 && st % 8 == 0 && sh % 8 == 0;
 }
 
+// Segment tables: rows [seg_start[s], seg_start[s+1]) are segment s, its first
+// seg_text_len[s] rows text, the first seg_text_valid[s] of those unpadded.
+int check_segments(int n_seg, const int32_t* start, const int32_t* text_len, const int32_t* text_valid,
+                   int64_t n) {
+  if (!start || !text_len || !text_valid) return fail(SEGC_EINVAL, "NULL segment table");
+  if (start[0] != 0) return fail(SEGC_EINVAL, "seg_start[0] must be 0");
+  if (start[n_seg] != n) return fail(SEGC_EINVAL, "seg_start[n_seg] = %d != %lld rows", start[n_seg], (long long)n);
+  for (int s = 0; s < n_seg; ++s) {
+    const int len = start[s + 1] - start[s];
+    if (len < 0) return fail(SEGC_EINVAL, "seg_start not ascending at %d", s);
+    if (text_len[s] < 0 || text_len[s] > len)
+      return fail(SEGC_EINVAL, "segment %d: text_len %d outside [0, %d]", s, text_len[s], len);
+    if (text_valid[s] < 0 || text_valid[s] > text_len[s])
+      return fail(SEGC_EINVAL, "segment %d: text_valid %d > text_len %d", s, text_valid[s], text_len[s]);
+  }
+  return SEGC_OK;
+}
+
+// Every query must see at least one key (else its softmax is undefined).
+int check_visible(int n_seg, const int32_t* start, const int32_t* text_len, const int32_t* text_valid,
+                  int64_t n_hist_rows) {
+  int64_t earlier_video = 0;
+  for (int s = 0; s < n_seg; ++s) {
+    const int len = start[s + 1] - start[s];
+    const int64_t visible = n_hist_rows + earlier_video + text_valid[s] + (len - text_len[s]);
+    if (len > 0 && visible == 0) return fail(SEGC_EINVAL, "segment %d has no visible key", s);
+    earlier_video += len - text_len[s];
+  }
+  return SEGC_OK;
+}
+
+
 int check_cache(const segc_cache* c) {
   if (!c) return fail(SEGC_EINVAL, "cache descriptor is NULL");
   if (c->dtype != SEGC_BF16 && c->dtype != SEGC_INT8)
@@ -203,26 +235,14 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
   if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->k_stride_tok, a->k_stride_head) ||
       !strides_ok(a->v_stride_tok, a->v_stride_head) || !strides_ok(a->o_stride_tok, a->o_stride_head))
     return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
-  if (!a->seg_start || !a->seg_text_len || !a->seg_text_valid)
-    return fail(SEGC_EINVAL, "NULL segment table");
-  if (a->seg_start[0] != 0) return fail(SEGC_EINVAL, "seg_start[0] must be 0");
-  if (a->seg_start[a->n_seg] != a->n_cur)
-    return fail(SEGC_EINVAL, "seg_start[n_seg] = %d != n_cur", a->seg_start[a->n_seg]);
-  for (int s = 0; s < a->n_seg; ++s) {
-    const int len = a->seg_start[s + 1] - a->seg_start[s];
-    if (len < 0) return fail(SEGC_EINVAL, "seg_start not ascending at %d", s);
-    if (a->seg_text_len[s] < 0 || a->seg_text_len[s] > len)
-      return fail(SEGC_EINVAL, "segment %d: text_len %d outside [0, %d]", s, a->seg_text_len[s], len);
-    if (a->seg_text_valid[s] < 0 || a->seg_text_valid[s] > a->seg_text_len[s])
-      return fail(SEGC_EINVAL, "segment %d: text_valid %d > text_len %d", s, a->seg_text_valid[s],
-                  a->seg_text_len[s]);
-  }
+  int rc = check_segments(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, a->n_cur);
+  if (rc) return rc;
   if (a->n_hist < 0) return fail(SEGC_EINVAL, "n_hist < 0");
   int64_t n_hist_rows = 0;
   int hist_int8 = 0;
   if (a->n_hist > 0) {
     if (!a->cache) return fail(SEGC_EINVAL, "n_hist > 0 without a cache");
-    int rc = check_cache(a->cache);
+    rc = check_cache(a->cache);
     if (rc) return rc;
     if (a->cache->n_heads != a->n_heads)
       return fail(SEGC_EINVAL, "cache has %d heads, call has %d", a->cache->n_heads, a->n_heads);
@@ -233,14 +253,8 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
     if (n_hist_rows > (int64_t)1 << 30) return fail(SEGC_EINVAL, "history too long");
     hist_int8 = a->cache->dtype == SEGC_INT8;
   }
-  // every query must see at least one key
-  int64_t earlier_video = 0;
-  for (int s = 0; s < a->n_seg; ++s) {
-    const int len = a->seg_start[s + 1] - a->seg_start[s];
-    const int64_t visible = n_hist_rows + earlier_video + a->seg_text_valid[s] + (len - a->seg_text_len[s]);
-    if (len > 0 && visible == 0) return fail(SEGC_EINVAL, "segment %d has no visible key", s);
-    earlier_video += len - a->seg_text_len[s];
-  }
+  rc = check_visible(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, n_hist_rows);
+  if (rc) return rc;
   if (a->n_cur == 0) return ok();
   if (!a->q || !a->k || !a->v || !a->o) return fail(SEGC_EINVAL, "NULL q/k/v/o");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
@@ -289,6 +303,91 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
   p.sm_scale = a->sm_scale;
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
   return hip_status(segc::launch_attn(p, (hipStream_t)stream), "segcausal_joint_attn launch");
+}
+
+int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
+  if (!a) return fail(SEGC_EINVAL, "args is NULL");
+  if (a->head_dim != SEGC_HEAD_DIM) return fail(SEGC_EUNSUPPORTED, "head_dim %d != 128", a->head_dim);
+  if (a->n_seg < 1 || a->n_seg > SEGC_MAX_SEG)
+    return fail(SEGC_EUNSUPPORTED, "n_seg %d outside [1, %d]", a->n_seg, SEGC_MAX_SEG);
+  if (a->n < 0 || a->n >= (int64_t)1 << 30) return fail(SEGC_EINVAL, "n out of range");
+  if (a->n_heads < 1 || a->n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
+    return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
+  const int64_t st[8][2] = {{a->q_stride_tok, a->q_stride_head},   {a->k_stride_tok, a->k_stride_head},
+                            {a->v_stride_tok, a->v_stride_head},   {a->o_stride_tok, a->o_stride_head},
+                            {a->do_stride_tok, a->do_stride_head}, {a->dq_stride_tok, a->dq_stride_head},
+                            {a->dk_stride_tok, a->dk_stride_head}, {a->dv_stride_tok, a->dv_stride_head}};
+  for (int i = 0; i < 8; ++i)
+    if (!strides_ok(st[i][0], st[i][1]))
+      return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+  int rc = check_segments(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, a->n);
+  if (rc) return rc;
+  rc = check_visible(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, 0);
+  if (rc) return rc;
+  if (a->n == 0) return ok();
+  const void* ptr[8] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv};
+  for (int i = 0; i < 8; ++i) {
+    if (!ptr[i]) return fail(SEGC_EINVAL, "NULL q/k/v/o/dout/dq/dk/dv");
+    if (!aligned16(ptr[i])) return fail(SEGC_EINVAL, "q/k/v/o/dout/dq/dk/dv must be 16-byte aligned");
+  }
+  if (!a->lse || !a->delta) return fail(SEGC_EINVAL, "NULL lse/delta");
+  if (((uintptr_t)a->lse & 3u) || ((uintptr_t)a->delta & 3u))
+    return fail(SEGC_EINVAL, "lse/delta must be 4-byte aligned");
+  // outputs are written while inputs are still read: an output that starts
+  // where another argument starts is an in-place call, which this computation
+  // cannot do (interleaved views, e.g. one [n][3][H][128] buffer, are fine)
+  const void* all[10] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse, a->delta};
+  const char* names[10] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv", "lse", "delta"};
+  const int outs[4] = {5, 6, 7, 9};
+  for (int oi = 0; oi < 4; ++oi)
+    for (int j = 0; j < 10; ++j)
+      if (j != outs[oi] && all[j] == all[outs[oi]])
+        return fail(SEGC_EINVAL, "%s and %s share a base pointer (in-place is not supported)",
+                    names[outs[oi]], names[j]);
+
+  segc::AttnBwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t*)a->q;
+  p.k = (const uint16_t*)a->k;
+  p.v = (const uint16_t*)a->v;
+  p.o = (const uint16_t*)a->o;
+  p.dout = (const uint16_t*)a->dout;
+  p.dq = (uint16_t*)a->dq;
+  p.dk = (uint16_t*)a->dk;
+  p.dv = (uint16_t*)a->dv;
+  p.lse = a->lse;
+  p.delta = a->delta;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.k_st = a->k_stride_tok;
+  p.k_sh = a->k_stride_head;
+  p.v_st = a->v_stride_tok;
+  p.v_sh = a->v_stride_head;
+  p.o_st = a->o_stride_tok;
+  p.o_sh = a->o_stride_head;
+  p.do_st = a->do_stride_tok;
+  p.do_sh = a->do_stride_head;
+  p.dq_st = a->dq_stride_tok;
+  p.dq_sh = a->dq_stride_head;
+  p.dk_st = a->dk_stride_tok;
+  p.dk_sh = a->dk_stride_head;
+  p.dv_st = a->dv_stride_tok;
+  p.dv_sh = a->dv_stride_head;
+  p.n = (int32_t)a->n;
+  p.n_heads = a->n_heads;
+  p.n_seg = a->n_seg;
+  bool needs_mask = a->n_seg > 1;
+  for (int s = 0; s <= a->n_seg; ++s) p.seg_start[s] = a->seg_start[s];
+  for (int s = 0; s < a->n_seg; ++s) {
+    p.seg_text_len[s] = a->seg_text_len[s];
+    p.seg_text_valid[s] = a->seg_text_valid[s];
+    needs_mask = needs_mask || a->seg_text_valid[s] < a->seg_text_len[s];
+  }
+  p.needs_mask = needs_mask;
+  p.sm_scale = a->sm_scale;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  return hip_status(segc::launch_attn_bwd(p, (hipStream_t)stream), "segcausal_joint_attn_bwd launch");
 }
 
 }  // extern "C"

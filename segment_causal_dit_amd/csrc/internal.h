@@ -87,4 +87,31 @@ struct AttnParams {
 };
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 
+// Gradients of the packed form (no history): delta = rowsum(do * o), then
+// dq, and dk with dv, from q, k, v, do and the forward's natural-log lse.
+struct AttnBwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const float* lse;          // [n_heads][n]
+  float* delta;              // [n_heads][n], written by the first kernel
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;       // elements
+  int64_t do_st, do_sh, dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh;
+  int32_t n;
+  int32_t n_heads;
+  int32_t n_seg;
+  int32_t needs_mask;        // segment structure beyond one unpadded segment
+  float sm_scale;
+  float scale_log2;          // sm_scale * log2(e)
+  int32_t seg_start[kMaxSeg + 1];
+  int32_t seg_text_len[kMaxSeg];
+  int32_t seg_text_valid[kMaxSeg];
+};
+hipError_t launch_attn_bwd(const AttnBwdParams& p, hipStream_t s);
+
 }  // namespace segc

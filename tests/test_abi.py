@@ -201,3 +201,62 @@ def test_attn_rejects_bad_segments(segs, n_cur):
 def test_attn_noop_and_null_args():
     assert lib.segcausal_joint_attn(None, None) == 1
     assert _attn(segs=((0, 0, 0),), n_cur=0, q=None, k=None, v=None, o=None) == 0
+
+
+# ----------------------------------------------------- attention backward ----
+
+FAKE2 = 0x20000000        # more aligned stand-ins, spaced so the spans never meet
+_BWD_PTRS = ("q", "k", "v", "o", "dout", "dq", "dk", "dv")
+
+
+def _attn_bwd(segs=((0, 16, 16),), n=64, **kw):
+    starts = [s[0] for s in segs] + [n]
+    ss = (ctypes.c_int32 * len(starts))(*starts)
+    tl = (ctypes.c_int32 * max(1, len(segs)))(*[s[1] for s in segs])
+    tv = (ctypes.c_int32 * max(1, len(segs)))(*[s[2] for s in segs])
+    ptrs = [FAKE2 + i * 0x1000000 for i in range(len(_BWD_PTRS))]
+    a = sc.SegcAttnBwdArgs(*(ptrs + [256, 128] * 8 +
+                             [FAKE2 + 8 * 0x1000000, FAKE2 + 9 * 0x1000000, n, 2, 128, len(segs), 0,
+                              ss, tl, tv, 0.088]))
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return lib.segcausal_joint_attn_bwd(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), 2), (dict(n_seg=0), 2), (dict(n_seg=17), 2),
+    (dict(n=-1), 1), (dict(n=1 << 30), 1), (dict(n_heads=0), 1), (dict(sm_scale=0.0), 1),
+    (dict(sm_scale=float("nan")), 1), (dict(q_stride_tok=100), 1), (dict(dv_stride_head=-8), 1),
+    (dict(do_stride_tok=4), 1), (dict(q=None), 1), (dict(dout=None), 1), (dict(dk=FAKE2 + 8), 1),
+    (dict(lse=None), 1), (dict(delta=None), 1), (dict(lse=FAKE2 + 2), 1),
+    (dict(delta=FAKE2 + 9 * 0x1000000 + 1), 1),
+    (dict(dq=FAKE2), 1),                         # dq in place of q
+    (dict(dv=FAKE2 + 6 * 0x1000000), 1),         # dv and dk the same buffer
+    (dict(delta=FAKE2 + 3 * 0x1000000), 1),      # delta in place of o
+    (dict(dk=FAKE2 + 8 * 0x1000000), 1),         # dk in place of lse
+])
+def test_attn_bwd_rejects(kw, code):
+    assert _attn_bwd(**kw) == code
+    assert lib.segcausal_last_error().decode()
+
+
+@pytest.mark.parametrize("segs,n", [
+    (((1, 0, 0),), 64), (((0, 16, 17),), 64), (((0, 65, 10),), 64),
+    (((0, 4, 4), (50, 2, 2), (40, 0, 0)), 64),
+    (((0, 8, 0),), 8),                           # only padded text: no visible key
+    (((0, 8, 8), (8, 8, 0)), 16),                # second segment: only padded text
+])
+def test_attn_bwd_rejects_bad_segments(segs, n):
+    assert _attn_bwd(segs=segs, n=n) == 1
+
+
+def test_attn_bwd_noop_and_null_args():
+    assert lib.segcausal_joint_attn_bwd(None, None) == 1
+    assert _attn_bwd(segs=((0, 0, 0),), n=0, q=None, k=None, v=None, o=None, dout=None,
+                     dq=None, dk=None, dv=None, lse=None, delta=None) == 0
+    # the binding checks shapes before the library is reached
+    import torch
+    x = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    lse = torch.zeros(2, 4)
+    with pytest.raises(ValueError):
+        sc.segcausal_joint_attn_bwd(x, x, x[:3], x, x, lse, [(0, 0, 0)], 0.088)

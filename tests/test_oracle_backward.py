@@ -57,3 +57,34 @@ def test_invisible_keys_get_no_gradient():
     q, k, v, do = _inputs(6)
     _, dk, dv = oracle.joint_attn_backward(q, k, v, SEGS, do)
     assert not np.any(dk[8]) and not np.any(dv[8])
+
+
+def test_key_gradient_sums_to_zero():
+    # ds sums to zero over each query row, so sum_j dk_j = scale sum_i q_i * 0
+    q, k, v, do = _inputs(7)
+    _, dk, _ = oracle.joint_attn_backward(q, k, v, SEGS, do, sm_scale=0.8)
+    assert np.max(np.abs(dk.sum(axis=0))) <= 1e-12
+
+
+def test_chunking_does_not_change_gradients():
+    q, k, v, do = _inputs(8)
+    a = oracle.joint_attn_backward(q, k, v, SEGS, do, chunk=512)
+    b = oracle.joint_attn_backward(q, k, v, SEGS, do, chunk=3)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=0, atol=1e-13)
+
+
+def test_dq_rows_match_central_differences():
+    # the sampled-row form, pinned on its own: perturb q of the chosen rows
+    q, k, v, do = _inputs(9)
+    rows = [0, 4, 8, 11, 16]
+    got = oracle.joint_attn_dq_rows(q, k, v, SEGS, do, rows, sm_scale=0.6)
+    eps = 1e-6
+    for ri, r in enumerate(rows):
+        for hd in range(H):
+            for c in range(D):
+                qp, qm = q.copy(), q.copy()
+                qp[r, hd, c] += eps
+                qm[r, hd, c] -= eps
+                fd = (_loss(qp, k, v, do, 0.6) - _loss(qm, k, v, do, 0.6)) / (2 * eps)
+                assert abs(fd - got[ri, hd, c]) <= 1e-6 * (1 + abs(fd)), (r, hd, c)

@@ -15,7 +15,7 @@ news page, the five-turn gallery clip). Seed 42 is the pages' default seed
 (model card, standard settings table).
 
 Recipe: numpy PCG64 seeded with 42 + k (k = 0 q, 1 k, 2 v, 3 history k,
-4 history v, 5 extra draws), float32 N(0, 1) draws rounded to bf16 (nearest,
+4 history v, 5 and 6 INT8 cache draws, 7 upstream gradient), float32 N(0, 1) draws rounded to bf16 (nearest,
 ties to even). Q is multiplied by `q_scale` before rounding. Trained
 activations do not exist here, so unit-variance draws stand in for them.
 """
@@ -151,7 +151,32 @@ VARIANTS = {
                           q_scale=_INV_SQRT_D),
 }
 
-ALL = dict(CONFIGS, **VARIANTS)
+# Packed training form (segment forcing): every segment present, no cache.
+# A segment is 256 text rows + 30 latent frames of 22x40 ("Hy-Nomas Explained
+# ...", the section on the latent math: 30 frames of 880 tokens per segment);
+# 13 of them (346,528 rows) fill the 360,000-row packing limit of the
+# fine-tuning recipe ("The training recipe"). The valid text lengths are
+# synthetic: prompts are padded to 256 rows.
+_TRAIN_VALID = (256, 201, 256, 143, 256, 256, 77, 256, 230, 256, 256, 164, 256)
+TRAIN = {
+    "train13": Config("train13", 16, _FULL,
+                      tuple(SegSpec(256, tv, 30, 30 * i) for i, tv in enumerate(_TRAIN_VALID)),
+                      q_scale=_INV_SQRT_D),
+    # small packed forms for gradient parity: ragged tails, padded text, a
+    # segment without text and one that is text only
+    "bwd_small": Config("bwd_small", 2, (8, 9),
+                        (SegSpec(37, 30, 2, 0), SegSpec(20, 20, 3, 2), SegSpec(0, 0, 2, 5),
+                         SegSpec(16, 5, 1, 7)), sm_scale=_INV_SQRT_D),
+    # full-size frames, four short segments: dozens of workgroups per head
+    "bwd_mid": Config("bwd_mid", 2, _FULL,
+                      (SegSpec(64, 64, 2, 0), SegSpec(64, 40, 2, 2), SegSpec(64, 7, 2, 4),
+                       SegSpec(64, 64, 2, 6)), q_scale=_INV_SQRT_D),
+    "bwd_one": Config("bwd_one", 3, (10, 13), (SegSpec(0, 0, 5, 0),), sm_scale=_INV_SQRT_D),
+    "bwd_text": Config("bwd_text", 2, (6, 7), (SegSpec(64, 64, 4, 0), SegSpec(64, 33, 0, 4),
+                                               SegSpec(1, 1, 3, 4)), q_scale=_INV_SQRT_D),
+}
+
+ALL = dict(CONFIGS, **VARIANTS, **TRAIN)
 
 
 # ---------------------------------------------------------------- draws ----
@@ -223,6 +248,14 @@ def make_inputs(cfg):
     slot_t[:nh] = np.asarray(cfg.hist_t, dtype=np.int32)
     return Inputs(cfg, q, k, v, video_rows, pos, hist_k, hist_v, hist_pos, slot_t,
                   cfg.segment_rows())
+
+
+def upstream_grad(cfg):
+    """bf16 bits [n_cur, H, D] of an upstream gradient dL/do: N(0, 1) draws
+    from PCG64(42 + 7)."""
+    if isinstance(cfg, str):
+        cfg = ALL[cfg]
+    return normal_bf16(7, (cfg.n_cur, cfg.n_heads, HEAD_DIM))
 
 
 def direct_int8_cache(cfg, frames):
