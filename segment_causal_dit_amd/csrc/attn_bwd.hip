@@ -51,9 +51,9 @@ constexpr int RW = BN / NSTAGE;
 constexpr int QW = 8;                      // dQ: waves per workgroup
 constexpr int QT = QW * 64;
 constexpr int QBM = 32 * QW;               // dQ: query rows per workgroup
-constexpr int KW = 4;                      // dK/dV: waves per workgroup
+constexpr int KW = 8;                      // dK/dV: waves per workgroup
 constexpr int KT = KW * 64;
-constexpr int KBN = 32 * KW;               // dK/dV: keys per workgroup
+constexpr int KBN = 128;                   // dK/dV: keys per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -350,11 +350,66 @@ __global__ __launch_bounds__(QT, 2) void dq_kernel(AttnBwdParams p) {
 
 // ------------------------------------------------------------------- dK/dV ----
 
-__global__ __launch_bounds__(KT, 1) void dkdv_kernel(AttnBwdParams p) {
+// Staging wave w of `nwaves` loads rows [rpw w, rpw w + rpw) of a tile of two
+// row-major tensors starting at row0 into dstA / dstB (rows past nvalid
+// repeat the last valid row).
+template <int RPW>
+__device__ inline void stage_pair(const uint16_t* a, int64_t a_st, const uint16_t* b, int64_t b_st,
+                                  int row0, int nvalid, int w, int lane, char* dstA, char* dstB) {
+  const char* ar[RPW / 4];
+  const char* br[RPW / 4];
+#pragma unroll
+  for (int e = 0; e < RPW / 4; ++e) {
+    const int r = row0 + min(RPW * w + 4 * e + (lane >> 4), nvalid - 1);
+    ar[e] = (const char*)(a + (int64_t)r * a_st);
+    br[e] = (const char*)(b + (int64_t)r * b_st);
+  }
+#pragma unroll
+  for (int e = 0; e < RPW / 4; ++e) {
+    const int row = RPW * w + 4 * e + (lane >> 4);
+    const int pc = lane & 15;
+    dload16(ar[e] + ((pc ^ swz(row)) << 4), dstA + (RPW * w + 4 * e) * 256);
+    dload16(br[e] + ((pc ^ swz(row)) << 4), dstB + (RPW * w + 4 * e) * 256);
+  }
+}
+
+// out[db] += T^T[32 db + ..][rows rbase + ..] pk[..]: as tileT_x_packed over
+// the 32 tile rows from rbase (two 16-row chunks).
+__device__ inline void tileT_x_packed32(const char* tile, int rbase, const u32x4 (&pk)[2], int lane, int hh,
+                                        f32x16 (&out)[4]) {
+  const int gi = lane & 15;
+  const int hb = ((gi & 3) >> 1) | (((lane >> 4) & 1) << 1);
+  const int r0 = rbase + 4 * hh + (gi >> 2);
+  const int sub = 8 * (gi & 1);
+#pragma unroll
+  for (int ck = 0; ck < 2; ++ck) {
+    const bf16x8 pb = as_bf16x8(pk[ck]);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tile + t_off(16 * ck + r0, 4 * db + hb) + sub));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tile + t_off(16 * ck + r0 + 8, 4 * db + hb) + sub));
+      const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      out[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb, out[db], 0, 0, 0);
+    }
+  }
+}
+
+constexpr int KV_BYTES = 2 * KBN * D * 2;              // K and V rows of the workgroup's keys
+constexpr int KLDS_BYTES = KV_BYTES + 2 * BUF_BYTES;
+static_assert(KW == 8 && KBN == 128, "dK/dV: 4 key groups x 2 query halves");
+static_assert(4 * 2 * 16384 <= KLDS_BYTES, "room for the partial sums of the wave pairs");
+
+// Wave w owns keys 32 (w & 3) .. + 31 of the workgroup and query rows
+// 32 (w >> 2) .. + 31 of every 64-row tile; the two waves of a key group add
+// their partial dK and dV through LDS at the end.
+__global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w & 3, qh = w >> 2;
   const int lr = lane & 31, hh = lane >> 5;
   // the first key tiles are seen by the most queries: they go first
   const int ktile = blockIdx.x / p.n_heads;
@@ -367,17 +422,15 @@ __global__ __launch_bounds__(KT, 1) void dkdv_kernel(AttnBwdParams p) {
   const bool wg_video = all_video(p, j0, j1);
   const int wg_kseg_last = seg_of(p, j1 - 1);
 
-  const int krow = j0 + 32 * w + lr;
+  const int krow = j0 + 32 * kg + lr;
   const bool kok = krow < p.n;
   int klo, khi;
   key_range(p, krow, klo, khi);
-  bf16x8 kf[8], vf[8];
-  load_frags(p.k + (int64_t)(kok ? krow : 0) * p.k_st + (int64_t)head * p.k_sh, kok, hh, kf);
-  load_frags(p.v + (int64_t)(kok ? krow : 0) * p.v_st + (int64_t)head * p.v_sh, kok, hh, vf);
-  __builtin_amdgcn_s_waitcnt(0);
 
   const uint16_t* qb = p.q + (int64_t)head * p.q_sh;
   const uint16_t* db_ = p.dout + (int64_t)head * p.do_sh;
+  char* const kv = smem;                      // K rows at 0, V rows at KBN * 256
+  char* const stage = smem + KV_BYTES;
   f32x16 dkacc[4], dvacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -398,50 +451,93 @@ __global__ __launch_bounds__(KT, 1) void dkdv_kernel(AttnBwdParams p) {
       ((int*)tb)[2 * BN + tid] = ok ? seg_of(p, r) : 0;
     }
   };
-  stage_rows(qb, p.q_st, db_, p.do_st, q_begin, min(BN, p.n - q_begin), w, lane, smem);
-  finish(q_begin, smem);
+  stage_pair<KBN / KW>(p.k + (int64_t)head * p.k_sh, p.k_st, p.v + (int64_t)head * p.v_sh, p.v_st, j0, j1 - j0,
+                       w, lane, kv, kv + KBN * 256);
+  stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q_begin, min(BN, p.n - q_begin), w, lane, stage + AOFF,
+                      stage + BOFF);
+  finish(q_begin, stage);
   __syncthreads();
+  const char* const ktile_l = kv + (32 * kg) * 256;
+  const char* const vtile_l = kv + (KBN + 32 * kg) * 256;
   for (int t = 0; t < n_qt; ++t) {
-    char* const cur = smem + (t & 1) * BUF_BYTES;
-    char* const nxt = smem + ((t + 1) & 1) * BUF_BYTES;
+    char* const cur = stage + (t & 1) * BUF_BYTES;
+    char* const nxt = stage + ((t + 1) & 1) * BUF_BYTES;
     const bool has_next = t + 1 < n_qt;
     const int q0 = q_begin + t * BN;
-    if (has_next) stage_rows(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt);
+    if (has_next)
+      stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt + AOFF,
+                          nxt + BOFF);
     const bool masked = p.needs_mask && !(wg_video && wg_kseg_last <= seg_of(p, q0));
-    f32x16 s[2], dp[2];
-    rows_x_frag(cur + AOFF, kf, lr, hh, s);     // S = Q K^T (queries in registers)
-    rows_x_frag(cur + BOFF, vf, lr, hh, dp);    // dP = dO V^T
+    // S = Q K^T and dP = dO V^T over this wave's 32 queries and 32 keys:
+    // queries in the accumulator rows, keys across lanes
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const char* qa = cur + AOFF;
+    const char* da = cur + BOFF;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8 aq = *(const bf16x8*)(qa + t_off(32 * qh + lr, 2 * dt + hh));
+      const bf16x8 bk = *(const bf16x8*)(ktile_l + t_off(lr, 2 * dt + hh));
+      const bf16x8 ad = *(const bf16x8*)(da + t_off(32 * qh + lr, 2 * dt + hh));
+      const bf16x8 bv = *(const bf16x8*)(vtile_l + t_off(lr, 2 * dt + hh));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
+    }
     const float* tb = (const float*)(cur + TOFF);
-    f32x16 pm[2], ds[2];
+    f32x16 pm, ds;
 #pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2)
+    for (int jq = 0; jq < 4; ++jq) {
+      const int r = 32 * qh + 8 * jq + 4 * hh;       // tile rows r .. r + 3
+      const f32x4 l4 = *(const f32x4*)(tb + r);
+      const f32x4 d4 = *(const f32x4*)(tb + BN + r);
+      const i32x4 g4 = *(const i32x4*)((const int*)tb + 2 * BN + r);
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int r = 32 * qb2 + 8 * jq + 4 * hh;       // rows r .. r + 3 of the tile
-        const f32x4 l4 = *(const f32x4*)(tb + r);
-        const f32x4 d4 = *(const f32x4*)(tb + BN + r);
-        i32x4 g4 = {0, 0, 0, 0};
-        if (masked) g4 = *(const i32x4*)((const int*)tb + 2 * BN + r);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float sv = s[qb2][4 * jq + jj];
-          if (masked && (g4[jj] < klo || g4[jj] > khi)) sv = -INFINITY;
-          const float pr = __builtin_amdgcn_exp2f(fmaf(sv, c, -l4[jj]));
-          pm[qb2][4 * jq + jj] = pr;
-          ds[qb2][4 * jq + jj] = pr * (dp[qb2][4 * jq + jj] - d4[jj]);
-        }
+      for (int jj = 0; jj < 4; ++jj) {
+        const bool vis = !masked || (g4[jj] >= klo && g4[jj] <= khi);
+        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[4 * jq + jj], c, -l4[jj])) : 0.0f;
+        pm[4 * jq + jj] = pr;
+        ds[4 * jq + jj] = pr * (dp[4 * jq + jj] - d4[jj]);
       }
-    u32x4 pkp[4], pkd[4];
-    pack_rows(pm, pkp);
-    pack_rows(ds, pkd);
-    tileT_x_packed(cur + BOFF, pkp, lane, hh, dvacc);   // dV^T += dO^T P
-    tileT_x_packed(cur + AOFF, pkd, lane, hh, dkacc);   // dK^T += Q^T dS
+    }
+    u32x4 pkp[2], pkd[2];
+#pragma unroll
+    for (int ck = 0; ck < 2; ++ck)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pkp[ck][e] = pack_bf16(pm[8 * ck + 2 * e], pm[8 * ck + 2 * e + 1]);
+        pkd[ck][e] = pack_bf16(ds[8 * ck + 2 * e], ds[8 * ck + 2 * e + 1]);
+      }
+    tileT_x_packed32(da, 32 * qh, pkp, lane, hh, dvacc);   // dV^T += dO^T P
+    tileT_x_packed32(qa, 32 * qh, pkd, lane, hh, dkacc);   // dK^T += Q^T dS
     if (has_next) finish(q0 + BN, nxt);
     __syncthreads();
   }
-  if (kok) {
-    store_row(p.dk + (int64_t)krow * p.dk_st + (int64_t)head * p.dk_sh, hh, dkacc, p.sm_scale);
-    store_row(p.dv + (int64_t)krow * p.dv_st + (int64_t)head * p.dv_sh, hh, dvacc, 1.0f);
+  // pair reduction: the second-half wave hands over its dV, the first-half
+  // wave its dK; each then finishes one of the two
+  float* const red = (float*)(smem + kg * 32768);
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[(db * 16 + j) * 64 + lane] = dvacc[db][j];
+  } else {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) red[4096 + (db * 16 + j) * 64 + lane] = dkacc[db][j];
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dvacc[db][j] += red[(db * 16 + j) * 64 + lane];
+    if (kok) store_row(p.dv + (int64_t)krow * p.dv_st + (int64_t)head * p.dv_sh, hh, dvacc, 1.0f);
+  } else {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dkacc[db][j] += red[4096 + (db * 16 + j) * 64 + lane];
+    if (kok) store_row(p.dk + (int64_t)krow * p.dk_st + (int64_t)head * p.dk_sh, hh, dkacc, p.sm_scale);
   }
 }
 
@@ -455,14 +551,14 @@ hipError_t launch_attn_bwd(const AttnBwdParams& p0, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  e = hipFuncSetAttribute((const void*)dkdv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, KLDS_BYTES);
   if (e != hipSuccess) return e;
   const int64_t nq = (int64_t)((p.n + QBM - 1) / QBM) * p.n_heads;
   hipLaunchKernelGGL(dq_kernel, dim3((unsigned)nq), dim3(QT), LDS_BYTES, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nk = (int64_t)((p.n + KBN - 1) / KBN) * p.n_heads;
-  hipLaunchKernelGGL(dkdv_kernel, dim3((unsigned)nk), dim3(KT), LDS_BYTES, s, p);
+  hipLaunchKernelGGL(dkdv_kernel, dim3((unsigned)nk), dim3(KT), KLDS_BYTES, s, p);
   return hipGetLastError();
 }
 
