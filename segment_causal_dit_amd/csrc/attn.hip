@@ -50,12 +50,14 @@
 //  * online softmax in base 2 with the rescale of O deferred until the running
 //    max grows by more than 2^8 (exact: the final division uses the same
 //    reference max);
-//  * masks are per tile: only tiles at a ragged end or with segment structure
-//    evaluate a per-element predicate from a 64-entry key table in LDS; keys
-//    of later segments than the workgroup's last query are never loaded;
+//  * masks are per tile: only tiles at a ragged end, or with text rows, or
+//    with video of a segment later than the workgroup's first query evaluate
+//    a per-element predicate from a 64-entry key table in LDS; keys of later
+//    segments than the workgroup's last query are never loaded;
 //  * workgroup ids are remapped so that each XCD (dispatched round-robin)
 //    works through contiguous query tiles of the same head, sharing K/V in L2.
 #include "internal.h"
+#include "segtab.h"
 
 namespace segc {
 namespace {
@@ -133,8 +135,23 @@ __device__ inline Tile tile_at(const AttnParams& p, int t, int cur_end) {
   return tl;
 }
 
-__device__ inline bool tile_masked(const AttnParams& p, const Tile& tl) {
-  return tl.nvalid < BN || (!tl.hist && p.needs_mask);
+// Mask state of the tiles, decided once per tile in ascending order: a tile
+// needs the per-element mask at a ragged end, or when it holds current rows
+// other than video of segments no later than the workgroup's first query
+// segment (segments ascend with rows, so every query of the workgroup sees
+// those). `kseg` tracks the segment of each current tile's first row for the
+// key table.
+struct MaskWalk {
+  FreeRuns free;
+  SegWalk kseg;
+  int qseg_first;
+};
+
+__device__ inline bool tile_masked(const AttnParams& p, const Tile& tl, MaskWalk& mw) {
+  if (!tl.hist) mw.kseg.at(p, tl.j0);
+  if (tl.nvalid < BN) return true;
+  if (tl.hist || !p.needs_mask) return false;
+  return !mw.free.free(p, BN, mw.qseg_first, tl.j0 / BN);
 }
 
 // Where a staging wave's group of RW consecutive tile rows lives. Uniform
@@ -320,27 +337,14 @@ __device__ inline void convert_group(const char* codes, const float* scales, cha
 
 // Visibility table of the tile's 64 keys: [lo, hi] range of query segments
 // that may see the key (lo > hi: nobody).
-__device__ inline void store_info(const AttnParams& p, const Tile& tl, int tid, int* info) {
+__device__ inline void store_info(const AttnParams& p, const Tile& tl, int tid, int* info, int sg) {
   if (tid >= BN) return;
-  int lo = 0xFFFF, hi = 0;
-  if (tid < tl.nvalid) {
-    if (tl.hist) {
-      lo = 0;
-      hi = 0xFFFF;
-    } else {
-      const int jc = tl.j0 + tid;
-      const int s = seg_of(p, jc);
-      const int ti = jc - p.seg_start[s];
-      if (ti >= p.seg_text_len[s]) {
-        lo = s;
-        hi = 0xFFFF;
-      } else if (ti < p.seg_text_valid[s]) {
-        lo = s;
-        hi = s;
-      }
-    }
-  }
-  info[tid] = lo | (hi << 16);
+  int v;
+  if (tl.hist)
+    v = (tid < tl.nvalid) ? (0xFFFF << 16) : 0xFFFF;
+  else
+    v = key_visibility(p, sg, tl.j0, BN, tl.j0 + tid, tid < tl.nvalid);
+  info[tid] = v;
 }
 
 // S^T (64 keys x 32 queries) = K Q^T from the K tile in LDS: the two key
@@ -456,7 +460,7 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
 // INT8 rows into bf16 (each wave converts exactly the rows it loaded), and
 // (wave 0) write the tile's key table when the tile needs a mask.
 __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, int lane, int tid,
-                                    char* buf, const char* raw, int newer) {
+                                    char* buf, const char* raw, int newer, bool masked, int sg) {
   // the direct loads are invisible to the compiler: wait in asm with a memory
   // clobber so that no read of the landed data is scheduled above the wait.
   // Loads complete in order: leaving the `newer` most recent ones (the next
@@ -472,7 +476,7 @@ __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, 
     convert_group<false>(raw + RAW_KC, sk, buf + KOFF, w, lane);
     convert_group<true>(raw + RAW_VC, sk + RW, buf + VOFF, w, lane);
   }
-  if (tile_masked(p, tl)) store_info(p, tl, tid, (int*)(buf + IOFF));
+  if (masked) store_info(p, tl, tid, (int*)(buf + IOFF), sg);
 }
 
 __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
@@ -494,6 +498,10 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   const int m0 = qtile * BM;
   const int wg_last = min(m0 + BM, p.n_cur) - 1;
   const int cur_end = p.seg_start[seg_of(p, wg_last) + 1];   // later keys are future for all
+  MaskWalk mw;
+  mw.qseg_first = seg_of(p, m0);
+  mw.free.init(p, BN, mw.qseg_first);
+  mw.kseg.init(p, 0);
   const int n_tiles = p.hist_tiles + (cur_end + BN - 1) / BN;
 
   // Q operands (B of S^T = K Q^T) and the query row's segment
@@ -528,10 +536,13 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   const bool stager = w < NSTAGE;
   char* const raw0 = smem + RAW0;
   char* const raw1 = smem + RAW0 + RAW_BYTES;
+  // every wave walks the mask state (scalar work); the next tile's decision
+  // is made after this tile's products are issued
+  bool mt = tile_masked(p, tile_at(p, 0, cur_end), mw);
   if (stager) {
     const Tile t0 = tile_at(p, 0, cur_end);
     stage_issue(p, t0, w, lane, head, smem, raw0);
-    stage_finish(p, t0, w, lane, tid, smem, raw0, 0);
+    stage_finish(p, t0, w, lane, tid, smem, raw0, 0, mt, mw.kseg.s);
     if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, raw1);
   }
   __syncthreads();
@@ -540,7 +551,6 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     char* const cur = smem + bc * BUF_BYTES;
     char* const nx1 = smem + (bc == NBUF - 1 ? 0 : bc + 1) * BUF_BYTES;
     char* const nx2 = smem + (bc == 0 ? NBUF - 1 : bc - 1) * BUF_BYTES;
-    const bool mt = tile_masked(p, tile_at(p, t, cur_end));
     const int* info = (const int*)(cur + IOFF);
     int issued = 0;
     if (stager && t + 2 < n_tiles)
@@ -549,9 +559,12 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     qk_tile(cur + KOFF, qf, lr, hh, sc);
     softmax_tile(sc, mt, info, qseg, hh, c, rs, o);
     pv_tile(cur + VOFF, sc, lane, hh, o, rs);
+    const bool mt_next = t + 1 < n_tiles && tile_masked(p, tile_at(p, t + 1, cur_end), mw);
     if (stager && t + 1 < n_tiles)
-      stage_finish(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued);
+      stage_finish(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued, mt_next,
+                   mw.kseg.s);
     __syncthreads();
+    mt = mt_next;
     bc = (bc == NBUF - 1) ? 0 : bc + 1;
   }
 

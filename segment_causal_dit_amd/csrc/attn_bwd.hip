@@ -34,6 +34,7 @@
 // pairs in which every key is video of a segment no later than the first
 // query's segment are fully visible and skip the per-element mask.
 #include "internal.h"
+#include "segtab.h"
 
 namespace segc {
 namespace {
@@ -292,28 +293,33 @@ __global__ __launch_bounds__(QT, 2) void dq_kernel(AttnBwdParams p) {
   for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
   const float c = p.scale_log2;
 
-  // key table of a tile: [lo, hi] query-segment range per key
-  auto finish = [&](int t, char* buf) {
-    dload_wait();
-    if (tid < BN) {
-      int lo, hi;
-      key_range(p, t * BN + tid, lo, hi);
-      ((int*)(buf + TOFF))[tid] = lo | (hi << 16);
-    }
+  // mask state of key tile t (decided once per tile, in order) and the key
+  // table of a masked tile: [lo, hi] query-segment range per key
+  FreeRuns fr;
+  fr.init(p, BN, qseg_first);
+  SegWalk kw;
+  kw.init(p, 0);
+  auto tile_masked = [&](int t) {
+    const int j0 = t * BN;
+    kw.at(p, j0);
+    return j0 + BN > cur_end || (p.needs_mask && !fr.free(p, BN, qseg_first, t));
   };
+  auto finish = [&](int t, char* buf, bool masked) {
+    dload_wait();
+    if (masked && tid < BN)
+      ((int*)(buf + TOFF))[tid] = key_visibility(p, kw.s, t * BN, BN, t * BN + tid, t * BN + tid < cur_end);
+  };
+  bool masked = tile_masked(0);
   if (stager) stage_rows(kb, p.k_st, vb, p.v_st, 0, min(BN, cur_end), w, lane, smem);
-  finish(0, smem);
+  finish(0, smem, masked);
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     char* const cur = smem + (t & 1) * BUF_BYTES;
     char* const nxt = smem + ((t + 1) & 1) * BUF_BYTES;
     const bool has_next = t + 1 < n_tiles;
     const int j0 = t * BN;
-    const int nvalid = min(BN, cur_end - j0);
     if (stager && has_next)
       stage_rows(kb, p.k_st, vb, p.v_st, j0 + BN, min(BN, cur_end - j0 - BN), w, lane, nxt);
-    const bool masked = nvalid < BN || (p.needs_mask && !(all_video(p, j0, j0 + BN) &&
-                                                          seg_of(p, j0 + BN - 1) <= qseg_first));
     f32x16 s[2], dp[2];
     rows_x_frag(cur + AOFF, qf, lr, hh, s);      // S^T = K Q^T
     rows_x_frag(cur + BOFF, df, lr, hh, dp);     // dP^T = V dO^T
@@ -342,8 +348,13 @@ __global__ __launch_bounds__(QT, 2) void dq_kernel(AttnBwdParams p) {
     u32x4 pk[4];
     pack_rows(ds, pk);
     tileT_x_packed(cur + AOFF, pk, lane, hh, acc);   // dQ^T += K^T dS^T
-    if (has_next) finish(t + 1, nxt);
+    bool masked_next = false;
+    if (has_next) {
+      masked_next = tile_masked(t + 1);
+      finish(t + 1, nxt, masked_next);
+    }
     __syncthreads();
+    masked = masked_next;
   }
   if (qok) store_row(p.dq + (int64_t)qrow * p.dq_st + (int64_t)head * p.dq_sh, hh, acc, p.sm_scale);
 }
@@ -439,8 +450,9 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
   }
   const float c = p.scale_log2;
 
-  // per-query tables of a tile: lse (log2 units; +inf past the end), delta, segment
-  auto finish = [&](int q0, char* buf) {
+  // per-query tables of a tile: lse (log2 units; +inf past the end), delta,
+  // segment (sg: the segment of the tile's first row)
+  auto finish = [&](int q0, char* buf, int sg) {
     dload_wait();
     if (tid < BN) {
       const int r = q0 + tid;
@@ -448,14 +460,20 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
       float* tb = (float*)(buf + TOFF);
       tb[tid] = ok ? p.lse[(int64_t)head * p.n + r] * kLog2e : INFINITY;
       tb[BN + tid] = ok ? p.delta[(int64_t)head * p.n + r] : 0.0f;
-      ((int*)tb)[2 * BN + tid] = ok ? seg_of(p, r) : 0;
+      ((int*)tb)[2 * BN + tid] = row_segment(p, sg, q0, BN, r);
     }
   };
+  // the tile needs the mask unless every key here is video of a segment no
+  // later than every query in it
+  SegWalk qw;
+  qw.init(p, q_begin);
+  auto tile_masked = [&](int qs) { return p.needs_mask && !(wg_video && wg_kseg_last <= qs); };
+  bool masked = tile_masked(qw.s);
   stage_pair<KBN / KW>(p.k + (int64_t)head * p.k_sh, p.k_st, p.v + (int64_t)head * p.v_sh, p.v_st, j0, j1 - j0,
                        w, lane, kv, kv + KBN * 256);
   stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q_begin, min(BN, p.n - q_begin), w, lane, stage + AOFF,
                       stage + BOFF);
-  finish(q_begin, stage);
+  finish(q_begin, stage, qw.s);
   __syncthreads();
   const char* const ktile_l = kv + (32 * kg) * 256;
   const char* const vtile_l = kv + (KBN + 32 * kg) * 256;
@@ -467,7 +485,6 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
     if (has_next)
       stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt + AOFF,
                           nxt + BOFF);
-    const bool masked = p.needs_mask && !(wg_video && wg_kseg_last <= seg_of(p, q0));
     // S = Q K^T and dP = dO V^T over this wave's 32 queries and 32 keys:
     // queries in the accumulator rows, keys across lanes
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -508,8 +525,14 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
       }
     tileT_x_packed32(da, 32 * qh, pkp, lane, hh, dvacc);   // dV^T += dO^T P
     tileT_x_packed32(qa, 32 * qh, pkd, lane, hh, dkacc);   // dK^T += Q^T dS
-    if (has_next) finish(q0 + BN, nxt);
+    bool masked_next = false;
+    if (has_next) {
+      const int qs = qw.at(p, q0 + BN);
+      masked_next = tile_masked(qs);
+      finish(q0 + BN, nxt, qs);
+    }
     __syncthreads();
+    masked = masked_next;
   }
   // pair reduction: the second-half wave hands over its dV, the first-half
   // wave its dK; each then finishes one of the two
