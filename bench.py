@@ -8,6 +8,8 @@ seeded synthetic tensors at the workload's shapes, resident in HBM before the
 timed region. Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline]
+  python bench.py --train [--steps K] [--warmup W]   (packed training form:
+      forward + backward of one layer's attention over 346,528 packed rows)
 """
 
 import argparse
@@ -176,6 +178,139 @@ def summarize_counters(cfg_name, fetch_dir, write_dir, out_path):
     print(json.dumps(summary))
 
 
+TRAIN_METRIC = "packed-form attention forward+backward TFLOP/s; % of bf16 MFMA roofline"
+
+
+def cpu_baseline_train(cfg, n_rows=16384):
+    """The fp64 oracle's gradients (which recompute the forward) on a bounded
+    sample of the packed workload: one head, the first n_rows rows of the
+    first segment (a packed sequence of its own)."""
+    import oracle
+    seg0 = cfg.segments[0]
+    shape = (n_rows, 1, HEAD_DIM)
+    q = oracle.bf16_bits_to_f64(workloads.normal_bf16(0, shape, cfg.q_scale))
+    k, v, do = (oracle.bf16_bits_to_f64(workloads.normal_bf16(i, shape)) for i in (1, 2, 7))
+    segs = [oracle.Segment(0, seg0.text_len, seg0.text_valid)]
+    pairs = n_rows * (n_rows - (seg0.text_len - seg0.text_valid))
+    t0 = time.perf_counter()
+    oracle.joint_attn_backward(q, k, v, segs, do, sm_scale=cfg.sm_scale)
+    dt = time.perf_counter() - t0
+    flops = 14 * HEAD_DIM * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count() or 1,
+            "kind": "oracle",
+            "sample": "forward+backward of the first %d rows of one segment, 1 head "
+                      "(numpy float64, %.1f s)" % (n_rows, dt)}
+
+
+def train_bench(args):
+    """Packed training form: one step = the forward (with lse) and the
+    backward of one layer's segment-causal attention over the packed
+    sequence (q and k rotated once, outside the timed region)."""
+    import torch
+    import segment_causal_dit_amd as sc
+
+    cfg = workloads.TRAIN["train13"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    h = cfg.n_heads
+    log("generating %s inputs" % cfg.name)
+    inp = workloads.make_inputs(cfg)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf(inp.q), bf(inp.k), bf(inp.v)
+    do = bf(workloads.upstream_grad(cfg))
+    pos = torch.from_numpy(inp.pos).to(dev)
+    pr = 0
+    g = cfg.tokens_per_frame
+    for (start, tl, _), sg in zip(inp.segments, cfg.segments):
+        n = sg.n_frames * g
+        sc.rope3d_apply(q[start + tl:start + tl + n], pos[pr:pr + n])
+        sc.rope3d_apply(k[start + tl:start + tl + n], pos[pr:pr + n])
+        pr += n
+    segs = inp.segments
+    o = torch.empty_like(q)
+    lse = torch.empty((h, cfg.n_cur), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream()
+    ev = {"fwd": [], "bwd": []}
+
+    def rec(name, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        ev[name].append((a, b))
+
+    def one_step():
+        rec("fwd", lambda: sc.segcausal_joint_attn(q, k, v, segs, cfg.sm_scale, out=o, lse=lse))
+        rec("bwd", lambda: sc.segcausal_joint_attn_bwd(q, k, v, o, do, lse, segs, cfg.sm_scale,
+                                                       dq=dq, dk=dk, dv=dv, delta=delta))
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    for k_ in ev:
+        ev[k_].clear()
+    log("timing %d steps" % args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["fwd"]]))
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev["bwd"]]))
+    pairs = cfg.visible_pairs() * h
+    fwd_flops, bwd_flops = 4 * HEAD_DIM * pairs, 10 * HEAD_DIM * pairs
+    step_tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+    bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    fwd_tflops = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    log("forward %.2f ms (%.1f%% of bf16 peak)  backward %.2f ms (%.1f%%)  step %.2f ms"
+        % (fwd_ms, 100 * fwd_tflops / PEAK_BF16_TFLOPS, bwd_ms, 100 * bwd_tflops / PEAK_BF16_TFLOPS,
+           ms_step))
+    line = {
+        "metric": TRAIN_METRIC,
+        "value": round(step_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: packed sequence of %d segments x (256 text + 30 frames of 22x40) = %d "
+                        "rows x %d heads x 128, no cache; forward (with lse) + backward "
+                        "(delta, dQ, dK/dV) of one layer's attention" % (cfg.name, len(cfg.segments),
+                                                                        cfg.n_cur, h),
+            "n_rows": cfg.n_cur, "segments": len(cfg.segments), "heads": h, "head_dim": HEAD_DIM,
+        },
+        "kernels_ms": {"forward": round(fwd_ms, 3), "backward": round(bwd_ms, 3)},
+        "flops_per_visible_pair": {"forward": 4 * HEAD_DIM, "backward": 10 * HEAD_DIM},
+        "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "backward call (delta + dQ + dK/dV)"},
+        "forward_roofline_frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        line["cpu_baseline"] = cpu_baseline_train(cfg)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +324,9 @@ def main():
     ap.add_argument("--counters-workload", action="store_true",
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--train", action="store_true",
+                    help="the packed training form instead: forward + backward of one layer's "
+                         "attention over 13 packed segments (346,528 rows)")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.config, args.summarize_counters[0], args.summarize_counters[1],
@@ -201,6 +339,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the attention would shard by heads; see the design notes).", file=sys.stderr)
         sys.exit(2)
+
+    if args.train:
+        train_bench(args)
+        return
 
     import torch
     import segment_causal_dit_amd as sc

@@ -147,11 +147,18 @@ struct MaskWalk {
   int qseg_first;
 };
 
+// kSeg = false: one unpadded segment (no per-element mask but at a ragged
+// end); the walk is compiled out, which keeps the loop's scalar state small.
+template <bool kSeg>
 __device__ inline bool tile_masked(const AttnParams& p, const Tile& tl, MaskWalk& mw) {
-  if (!tl.hist) mw.kseg.at(p, tl.j0);
-  if (tl.nvalid < BN) return true;
-  if (tl.hist || !p.needs_mask) return false;
-  return !mw.free.free(p, BN, mw.qseg_first, tl.j0 / BN);
+  if constexpr (!kSeg) {
+    return tl.nvalid < BN;
+  } else {
+    if (!tl.hist) mw.kseg.at(p, tl.j0);
+    if (tl.nvalid < BN) return true;
+    if (tl.hist) return false;
+    return !mw.free.free(p, BN, mw.qseg_first, tl.j0 / BN);
+  }
 }
 
 // Where a staging wave's group of RW consecutive tile rows lives. Uniform
@@ -337,10 +344,11 @@ __device__ inline void convert_group(const char* codes, const float* scales, cha
 
 // Visibility table of the tile's 64 keys: [lo, hi] range of query segments
 // that may see the key (lo > hi: nobody).
+template <bool kSeg>
 __device__ inline void store_info(const AttnParams& p, const Tile& tl, int tid, int* info, int sg) {
   if (tid >= BN) return;
   int v;
-  if (tl.hist)
+  if (!kSeg || tl.hist)
     v = (tid < tl.nvalid) ? (0xFFFF << 16) : 0xFFFF;
   else
     v = key_visibility(p, sg, tl.j0, BN, tl.j0 + tid, tid < tl.nvalid);
@@ -459,6 +467,7 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
 // Finish staging wave w's group of tile tl: wait for its direct loads, turn
 // INT8 rows into bf16 (each wave converts exactly the rows it loaded), and
 // (wave 0) write the tile's key table when the tile needs a mask.
+template <bool kSeg>
 __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, int lane, int tid,
                                     char* buf, const char* raw, int newer, bool masked, int sg) {
   // the direct loads are invisible to the compiler: wait in asm with a memory
@@ -476,9 +485,10 @@ __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, 
     convert_group<false>(raw + RAW_KC, sk, buf + KOFF, w, lane);
     convert_group<true>(raw + RAW_VC, sk + RW, buf + VOFF, w, lane);
   }
-  if (masked) store_info(p, tl, tid, (int*)(buf + IOFF), sg);
+  if (masked) store_info<kSeg>(p, tl, tid, (int*)(buf + IOFF), sg);
 }
 
+template <bool kSeg>
 __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -499,9 +509,13 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   const int wg_last = min(m0 + BM, p.n_cur) - 1;
   const int cur_end = p.seg_start[seg_of(p, wg_last) + 1];   // later keys are future for all
   MaskWalk mw;
-  mw.qseg_first = seg_of(p, m0);
-  mw.free.init(p, BN, mw.qseg_first);
-  mw.kseg.init(p, 0);
+  if constexpr (kSeg) {
+    mw.qseg_first = seg_of(p, m0);
+    mw.free.init(p, BN, mw.qseg_first);
+    mw.kseg.init(p, 0);
+  } else {
+    mw.kseg.s = 0;
+  }
   const int n_tiles = p.hist_tiles + (cur_end + BN - 1) / BN;
 
   // Q operands (B of S^T = K Q^T) and the query row's segment
@@ -538,11 +552,11 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   char* const raw1 = smem + RAW0 + RAW_BYTES;
   // every wave walks the mask state (scalar work); the next tile's decision
   // is made after this tile's products are issued
-  bool mt = tile_masked(p, tile_at(p, 0, cur_end), mw);
+  bool mt = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
   if (stager) {
     const Tile t0 = tile_at(p, 0, cur_end);
     stage_issue(p, t0, w, lane, head, smem, raw0);
-    stage_finish(p, t0, w, lane, tid, smem, raw0, 0, mt, mw.kseg.s);
+    stage_finish<kSeg>(p, t0, w, lane, tid, smem, raw0, 0, mt, mw.kseg.s);
     if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, raw1);
   }
   __syncthreads();
@@ -559,9 +573,9 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     qk_tile(cur + KOFF, qf, lr, hh, sc);
     softmax_tile(sc, mt, info, qseg, hh, c, rs, o);
     pv_tile(cur + VOFF, sc, lane, hh, o, rs);
-    const bool mt_next = t + 1 < n_tiles && tile_masked(p, tile_at(p, t + 1, cur_end), mw);
+    const bool mt_next = t + 1 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t + 1, cur_end), mw);
     if (stager && t + 1 < n_tiles)
-      stage_finish(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued, mt_next,
+      stage_finish<kSeg>(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued, mt_next,
                    mw.kseg.s);
     __syncthreads();
     mt = mt_next;
@@ -593,10 +607,13 @@ hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
   p.n_qtiles = (p.n_cur + BM - 1) / BM;
   const int64_t nwg = (int64_t)p.n_qtiles * p.n_heads;
   // more than 64 KB of dynamic LDS must be allowed explicitly (gfx950 has 160 KB per CU)
-  hipError_t e = hipFuncSetAttribute((const void*)attn_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  const void* fn = p.needs_mask ? (const void*)attn_kernel<true> : (const void*)attn_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p);
+  if (p.needs_mask)
+    hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p);
+  else
+    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p);
   return hipGetLastError();
 }
 
