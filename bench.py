@@ -10,6 +10,8 @@ timed region. Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--config c4] [--no-cpu-baseline]
   python bench.py --train [--steps K] [--warmup W]   (packed training form:
       forward + backward of one layer's attention over 346,528 packed rows)
+  python bench.py --archive [--steps K] [--warmup W] (CPU history archive:
+      window fetch and segment store over PCIe, overlap with attention)
 """
 
 import argparse
@@ -311,6 +313,146 @@ def train_bench(args):
     print(json.dumps(line), flush=True)
 
 
+ARCHIVE_METRIC = "history archive fetch GB/s (pinned host -> device frames); overlap with attention"
+PEAK_PCIE_GBS = 64.0         # MI355X host link: PCIe Gen5 x16, per direction
+
+
+def archive_bench(args):
+    """CPU history archive on the full frame geometry (16 heads x 880 tokens,
+    INT8 codes + fp32 scales, 3.72 MB per frame and layer): the fetch of an
+    18-frame window from pinned host memory, the store of one 8-frame
+    segment, and the fetch on a copy stream while the c3 attention (18 INT8
+    history frames + an 8-frame segment) runs on the main stream."""
+    import torch
+    import segment_causal_dit_amd as sc
+
+    cfg = workloads.CONFIGS["c3"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    h, g = cfg.n_heads, cfg.tokens_per_frame
+    window, seg_frames, n_arch = 18, 8, 72
+    frame_bytes = 2 * h * g * (HEAD_DIM + 4)
+    arch = sc.KVCache.archive(n_arch, h, g, "int8")
+    kc, vc, ks, vs = workloads.uniform_int8_cache(cfg, n_arch)
+    for t, a in zip((arch.k, arch.v, arch.k_scale, arch.v_scale), (kc, vc, ks, vs)):
+        t.copy_(torch.from_numpy(a))
+    del kc, vc, ks, vs
+    cache = sc.KVCache(cfg.n_slots + window, h, g, "int8", dev)
+    inp = workloads.make_inputs(cfg)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf(inp.q), bf(inp.k), bf(inp.v)
+    sc.kv_archive_fetch(arch, list(range(window)), cache, list(range(window)))
+    hist = torch.arange(window, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    seg = cfg.segments[0]
+    segs = [(0, seg.text_len, seg.text_valid)]
+    copy_stream = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    fetch_frames = list(range(30, 30 + window))            # older frames, re-entering the window
+    fetch_slots = list(range(cfg.n_slots, cfg.n_slots + window))
+    store_slots = list(range(seg_frames))
+    store_frames = list(range(n_arch - seg_frames, n_arch))
+
+    def timed(fn, stream):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        return a, b
+
+    def attn():
+        sc.segcausal_joint_attn(q, k, v, segs, cfg.sm_scale, cache=cache, hist_slots=hist, out=out)
+
+    def fetch():
+        sc.kv_archive_fetch(arch, fetch_frames, cache, fetch_slots, stream=copy_stream)
+
+    def store():
+        sc.kv_archive_store(cache, store_slots, arch, store_frames, stream=copy_stream)
+
+    for _ in range(args.warmup):
+        attn()
+        fetch()
+        store()
+    torch.cuda.synchronize()
+    res = {"fetch": [], "store": [], "attn": [], "attn_overlap": [], "fetch_overlap": []}
+    for _ in range(args.steps):
+        ev = timed(fetch, copy_stream)
+        torch.cuda.synchronize()
+        res["fetch"].append(ev[0].elapsed_time(ev[1]))
+        ev = timed(store, copy_stream)
+        torch.cuda.synchronize()
+        res["store"].append(ev[0].elapsed_time(ev[1]))
+        ev = timed(attn, main)
+        torch.cuda.synchronize()
+        res["attn"].append(ev[0].elapsed_time(ev[1]))
+        # both at once: the copy stream starts when the attention does
+        copy_stream.wait_stream(main)
+        ea = timed(attn, main)
+        ef = timed(fetch, copy_stream)
+        torch.cuda.synchronize()
+        res["attn_overlap"].append(ea[0].elapsed_time(ea[1]))
+        res["fetch_overlap"].append(ef[0].elapsed_time(ef[1]))
+    med = {k_: float(np.median(v_)) for k_, v_ in res.items()}
+    fetch_bytes, store_bytes = window * frame_bytes, seg_frames * frame_bytes
+    fetch_gbs = fetch_bytes / (med["fetch"] * 1e-3) / 1e9
+    store_gbs = store_bytes / (med["store"] * 1e-3) / 1e9
+    log("fetch %d frames %.3f ms (%.1f GB/s)  store %d frames %.3f ms (%.1f GB/s)  attention %.3f ms, "
+        "with a concurrent fetch %.3f ms (fetch %.3f ms)" % (window, med["fetch"], fetch_gbs, seg_frames,
+                                                              med["store"], store_gbs, med["attn"],
+                                                              med["attn_overlap"], med["fetch_overlap"]))
+    line = {
+        "metric": ARCHIVE_METRIC,
+        "value": round(fetch_gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med["fetch"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": "archive: %d-frame INT8 window of 16 heads x 880 tokens (codes + fp32 scales, "
+                               "%.2f MB per frame and layer) fetched from pinned host memory; store of an "
+                               "%d-frame segment; fetch overlapped with the c3 attention (18 INT8 history "
+                               "frames + 8-frame segment)" % (window, frame_bytes / 1e6, seg_frames)},
+        "store_gbs": round(store_gbs, 3),
+        "kernels_ms": {"fetch": round(med["fetch"], 4), "store": round(med["store"], 4),
+                       "attention": round(med["attn"], 4),
+                       "attention_with_concurrent_fetch": round(med["attn_overlap"], 4),
+                       "fetch_concurrent_with_attention": round(med["fetch_overlap"], 4)},
+        "roofline": {"bound": "pcie", "achieved": round(fetch_gbs, 3), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                     "frac": round(fetch_gbs / PEAK_PCIE_GBS, 4), "traffic": None,
+                     "kernel": "host-to-device DMA of the window"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        a_np = arch.k.numpy()
+        dst = np.zeros((window,) + a_np.shape[1:], a_np.dtype)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            for t in (arch.k, arch.v, arch.k_scale, arch.v_scale):
+                a_ = t.numpy()
+                oracle.move_frames(a_, fetch_frames, np.zeros((window,) + a_.shape[1:], a_.dtype),
+                                   list(range(window)))
+            reps += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(reps * fetch_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": "the oracle's indexed copy of the same %d frames in host memory, "
+                                          "%d repetitions in %.1f s" % (window, reps, dt)}
+        del dst
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +466,9 @@ def main():
     ap.add_argument("--counters-workload", action="store_true",
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--archive", action="store_true",
+                    help="the CPU history archive instead: window fetch / segment store over PCIe, and "
+                         "the fetch overlapped with an attention call")
     ap.add_argument("--train", action="store_true",
                     help="the packed training form instead: forward + backward of one layer's "
                          "attention over 13 packed segments (346,528 rows)")
@@ -342,6 +487,9 @@ def main():
 
     if args.train:
         train_bench(args)
+        return
+    if args.archive:
+        archive_bench(args)
         return
 
     import torch

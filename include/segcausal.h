@@ -155,6 +155,37 @@ int kv_window_dequant(const segc_cache* cache, const int32_t* slots, int32_t n_f
                       const segc_cache* out, void* stream);
 
 /*
+ * kv_archive_fetch / kv_archive_store -- move whole frames between a device
+ * cache and a history archive in pinned host memory.
+ * Source: model card, section "Single-GPU Low-Memory Inference" (up to 18
+ * historical frames on the GPU, older history archived on the CPU) and the
+ * model card's description of the per-layer cache reused as generation
+ * advances.
+ *
+ * The archive is a segc_cache whose k, v (and k_scale, v_scale for INT8)
+ * point to PINNED HOST memory (hipHostMalloc or an equivalent pinned
+ * allocation) in the cache layout, n_slots = its frame capacity. fetch copies
+ * archive frame archive_frames[i] into cache slot slots[i]; store copies cache
+ * slot slots[i] into archive frame archive_frames[i] (codes and scales,
+ * byte for byte). archive_frames and slots are HOST int32 arrays of n
+ * entries. Copies are asynchronous DMA on `stream` (a copy stream lets them
+ * overlap attention on another stream); runs of consecutive frames on both
+ * sides go as one copy per tensor. The caller keeps the host lists' contents
+ * only until the call returns, and the archive and cache alive and unchanged
+ * until the stream has run the copies.
+ * Errors: EINVAL on a bad descriptor, descriptors that differ in dtype,
+ *   heads or tokens_per_frame, n < 0, NULL lists, an index out of range, a
+ *   destination frame listed twice, an archive that is not pinned host
+ *   memory or a cache that is not device memory; EHIP if a copy cannot be
+ *   queued (earlier copies of the call may then have been queued).
+ *   n == 0 is a no-op.
+ */
+int kv_archive_fetch(const segc_cache* archive, const int32_t* archive_frames, const segc_cache* cache,
+                     const int32_t* slots, int32_t n, void* stream);
+int kv_archive_store(const segc_cache* cache, const int32_t* slots, const segc_cache* archive,
+                     const int32_t* archive_frames, int32_t n, void* stream);
+
+/*
  * window_select -- choose the cached frames the attention reads (host only).
  * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
  * (a bounded set of historical latent frames, default budget 18, excluding
@@ -292,7 +323,7 @@ const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 2)
+#define SEGC_ABI_VERSION ((1 << 16) | 3)
 
 #ifdef __cplusplus
 }

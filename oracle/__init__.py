@@ -22,6 +22,8 @@ describing Hy-Nomas:
   RTX 4090", section "How the RTX 4090 configuration saves memory".
 * The Explainer's section "The training recipe" (segment forcing on packed
   sequences) for the gradients of the packed form (attention_bwd.py).
+* The model card's "Single-GPU Low-Memory Inference" for the CPU history
+  archive (archive.py).
 
 Readings where the pages leave a step open are listed in each module.
 
@@ -36,6 +38,7 @@ from .rope import rope3d, rope3d_bf16, rope_frequencies
 from .quant import quantise_int8, dequantise_int8, dequantise_int8_bf16
 from .window import window_select, WindowError
 from .attention_bwd import joint_attn_backward, joint_attn_dq_rows
+from .archive import move_frames
 from .attention import (Segment, visible_mask, history_keys, joint_attn,
                         joint_attn_rows)
 
@@ -45,5 +48,5 @@ __all__ = [
     "quantise_int8", "dequantise_int8",
     "window_select", "WindowError",
     "Segment", "visible_mask", "history_keys", "joint_attn", "joint_attn_rows",
-    "dequantise_int8_bf16", "joint_attn_backward", "joint_attn_dq_rows",
+    "dequantise_int8_bf16", "joint_attn_backward", "joint_attn_dq_rows", "move_frames",
 ]

@@ -64,17 +64,19 @@ _lib.rope3d_apply.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp, _f64,
 _lib.kv_cache_append.argtypes = [ctypes.POINTER(SegcCache), _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
 _lib.kv_window_dequant.argtypes = [ctypes.POINTER(SegcCache), _vp, _i32, ctypes.POINTER(SegcCache), _vp]
 _lib.window_select.argtypes = [_pi32, _i32, _i32, _pi32, _pi32]
+_lib.kv_archive_fetch.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
+_lib.kv_archive_store.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
 _lib.segcausal_joint_attn_bwd.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
 _lib.segcausal_last_error.restype = ctypes.c_char_p
 _lib.segcausal_abi_version.restype = ctypes.c_int
 for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_joint_attn_bwd"):
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "segcausal_last_error",
-           "segcausal_abi_version")
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
+           "segcausal_last_error", "segcausal_abi_version")
 
 
 class SegcError(RuntimeError):
@@ -131,15 +133,16 @@ class KVCache:
     slot_t : host numpy int32 [n_slots], latent-frame index held by each slot
     """
 
-    def __init__(self, n_slots, n_heads, tokens_per_frame, dtype="int8", device="cuda"):
+    def __init__(self, n_slots, n_heads, tokens_per_frame, dtype="int8", device="cuda", pinned=False):
         shape = (n_slots, n_heads, tokens_per_frame, HEAD_DIM)
         self.int8 = dtype == "int8"
         tdt = torch.int8 if self.int8 else torch.bfloat16
-        self.k = torch.zeros(shape, dtype=tdt, device=device)
-        self.v = torch.zeros(shape, dtype=tdt, device=device)
+        kw = dict(device=device, pin_memory=True) if pinned else dict(device=device)
+        self.k = torch.zeros(shape, dtype=tdt, **kw)
+        self.v = torch.zeros(shape, dtype=tdt, **kw)
         if self.int8:
-            self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
-            self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+            self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, **kw)
+            self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, **kw)
         else:
             self.k_scale = self.v_scale = None
         self.slot_t = np.full(n_slots, -1, dtype=np.int32)
@@ -147,6 +150,11 @@ class KVCache:
                               tokens_per_frame, n_slots, 0, self.k.data_ptr(), self.v.data_ptr(),
                               self.k_scale.data_ptr() if self.int8 else None,
                               self.v_scale.data_ptr() if self.int8 else None)
+
+    @classmethod
+    def archive(cls, n_frames, n_heads, tokens_per_frame, dtype="int8"):
+        """A history archive: the cache layout in pinned host memory."""
+        return cls(n_frames, n_heads, tokens_per_frame, dtype, device="cpu", pinned=True)
 
     @property
     def n_slots(self):
@@ -184,6 +192,33 @@ def kv_window_dequant(cache, slots, out, stream=None):
     _check(_lib.kv_window_dequant(ctypes.byref(cache.desc), slots.data_ptr(), slots.shape[0],
                                   ctypes.byref(out.desc), _stream(stream)))
     return slots.shape[0]
+
+
+def _frame_list(x, name):
+    a = np.ascontiguousarray(x, dtype=np.int32)
+    if a.ndim != 1:
+        raise ValueError("%s must be 1-D" % name)
+    return a
+
+
+def kv_archive_fetch(archive, archive_frames, cache, slots, stream=None):
+    """Copy archive frames archive_frames[i] (pinned host) into cache slots
+    slots[i] (device), asynchronously on `stream`."""
+    af, sl = _frame_list(archive_frames, "archive_frames"), _frame_list(slots, "slots")
+    if len(af) != len(sl):
+        raise ValueError("archive_frames and slots differ in length")
+    _check(_lib.kv_archive_fetch(ctypes.byref(archive.desc), af.ctypes.data_as(_pi32), ctypes.byref(cache.desc),
+                                 sl.ctypes.data_as(_pi32), len(af), _stream(stream)))
+
+
+def kv_archive_store(cache, slots, archive, archive_frames, stream=None):
+    """Copy cache slots slots[i] (device) into archive frames archive_frames[i]
+    (pinned host), asynchronously on `stream`."""
+    af, sl = _frame_list(archive_frames, "archive_frames"), _frame_list(slots, "slots")
+    if len(af) != len(sl):
+        raise ValueError("archive_frames and slots differ in length")
+    _check(_lib.kv_archive_store(ctypes.byref(cache.desc), sl.ctypes.data_as(_pi32), ctypes.byref(archive.desc),
+                                 af.ctypes.data_as(_pi32), len(af), _stream(stream)))
 
 
 def window_select(slot_t, budget):

@@ -91,6 +91,79 @@ int check_cache(const segc_cache* c) {
   return SEGC_OK;
 }
 
+// Memory kind of [p, p + bytes) as HIP reports it at both ends (pinned host
+// memory, device memory, or neither).
+hipMemoryType memory_kind(const void* p, size_t bytes) {
+  hipPointerAttribute_t a, b;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipMemoryTypeUnregistered;
+  }
+  if (bytes > 1 && hipPointerGetAttributes(&b, (const char*)p + bytes - 1) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipMemoryTypeUnregistered;
+  }
+  if (bytes > 1 && b.type != a.type) return hipMemoryTypeUnregistered;
+  return a.type;
+}
+
+// Frame copies between two caches of one layout (one of them a pinned host
+// archive): element i moves frame src_idx[i] of src into frame dst_idx[i]
+// of dst. Runs of consecutive frames on both sides become one copy per tensor.
+int move_frames(const segc_cache* src, const int32_t* src_idx, const segc_cache* dst, const int32_t* dst_idx,
+                int32_t n, hipMemcpyKind kind, const char* what, void* stream) {
+  int rc = check_cache(src);
+  if (rc) return rc;
+  rc = check_cache(dst);
+  if (rc) return rc;
+  if (src->dtype != dst->dtype || src->n_heads != dst->n_heads || src->tokens_per_frame != dst->tokens_per_frame)
+    return fail(SEGC_EINVAL, "%s: archive and cache differ in dtype, heads or tokens_per_frame", what);
+  if (n < 0) return fail(SEGC_EINVAL, "%s: n < 0", what);
+  if (n == 0) return ok();
+  if (!src_idx || !dst_idx) return fail(SEGC_EINVAL, "%s: NULL frame list", what);
+  std::vector<int32_t> seen;
+  seen.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (src_idx[i] < 0 || src_idx[i] >= src->n_slots)
+      return fail(SEGC_EINVAL, "%s: source frame %d outside [0, %d)", what, src_idx[i], src->n_slots);
+    if (dst_idx[i] < 0 || dst_idx[i] >= dst->n_slots)
+      return fail(SEGC_EINVAL, "%s: destination frame %d outside [0, %d)", what, dst_idx[i], dst->n_slots);
+    seen.push_back(dst_idx[i]);
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+    return fail(SEGC_EINVAL, "%s: a destination frame appears twice", what);
+  const size_t rows = (size_t)src->n_heads * src->tokens_per_frame;
+  const size_t code_bytes = rows * SEGC_HEAD_DIM * (src->dtype == SEGC_INT8 ? 1 : 2);
+  const size_t scale_bytes = rows * sizeof(float);
+  const bool int8 = src->dtype == SEGC_INT8;
+  const segc_cache* host = kind == hipMemcpyHostToDevice ? src : dst;
+  const segc_cache* dev = kind == hipMemcpyHostToDevice ? dst : src;
+  const void* hp[4] = {host->k, host->v, host->k_scale, host->v_scale};
+  const void* dp[4] = {dev->k, dev->v, dev->k_scale, dev->v_scale};
+  const size_t fb[4] = {code_bytes, code_bytes, scale_bytes, scale_bytes};
+  for (int t = 0; t < (int8 ? 4 : 2); ++t) {
+    if (memory_kind(hp[t], fb[t] * host->n_slots) != hipMemoryTypeHost)
+      return fail(SEGC_EINVAL, "%s: the archive must be pinned host memory (hipHostMalloc)", what);
+    if (memory_kind(dp[t], fb[t] * dev->n_slots) != hipMemoryTypeDevice)
+      return fail(SEGC_EINVAL, "%s: the cache must be device memory", what);
+  }
+  char* const sp[4] = {(char*)src->k, (char*)src->v, (char*)src->k_scale, (char*)src->v_scale};
+  char* const tp[4] = {(char*)dst->k, (char*)dst->v, (char*)dst->k_scale, (char*)dst->v_scale};
+  for (int32_t i = 0; i < n;) {
+    int32_t j = i + 1;
+    while (j < n && src_idx[j] == src_idx[j - 1] + 1 && dst_idx[j] == dst_idx[j - 1] + 1) ++j;
+    const size_t frames = (size_t)(j - i);
+    for (int t = 0; t < (int8 ? 4 : 2); ++t) {
+      const hipError_t e = hipMemcpyAsync(tp[t] + fb[t] * dst_idx[i], sp[t] + fb[t] * src_idx[i], fb[t] * frames,
+                                          kind, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_status(e, what);
+    }
+    i = j;
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,6 +272,18 @@ int kv_window_dequant(const segc_cache* cache, const int32_t* slots, int32_t n_f
   p.rows_per_frame = (int32_t)rows_per_frame;
   p.n_rows = (int32_t)(rows_per_frame * n_frames);
   return hip_status(segc::launch_dequant(p, (hipStream_t)stream), "kv_window_dequant launch");
+}
+
+int kv_archive_fetch(const segc_cache* archive, const int32_t* archive_frames, const segc_cache* cache,
+                     const int32_t* slots, int32_t n, void* stream) {
+  return move_frames(archive, archive_frames, cache, slots, n, hipMemcpyHostToDevice, "kv_archive_fetch",
+                     stream);
+}
+
+int kv_archive_store(const segc_cache* cache, const int32_t* slots, const segc_cache* archive,
+                     const int32_t* archive_frames, int32_t n, void* stream) {
+  return move_frames(cache, slots, archive, archive_frames, n, hipMemcpyDeviceToHost, "kv_archive_store",
+                     stream);
 }
 
 int window_select(const int32_t* slot_t, int32_t n_slots, int32_t budget, int32_t* out_slots,

@@ -260,3 +260,40 @@ def test_attn_bwd_noop_and_null_args():
     lse = torch.zeros(2, 4)
     with pytest.raises(ValueError):
         sc.segcausal_joint_attn_bwd(x, x, x[:3], x, x, lse, [(0, 0, 0)], 0.088)
+
+
+# ------------------------------------------------------------ archive ----
+
+def _frames(*xs):
+    return (ctypes.c_int32 * max(1, len(xs)))(*xs)
+
+
+def _fetch(archive=None, af=(0, 1), cache=None, slots=(2, 3), n=None):
+    a = archive if archive is not None else _cache(n_slots=40)
+    c = cache if cache is not None else _cache()
+    return lib.kv_archive_fetch(ctypes.byref(a) if a != "null" else None, _frames(*af),
+                                ctypes.byref(c) if c != "null" else None, _frames(*slots),
+                                len(af) if n is None else n, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(archive="null"), dict(cache="null"),
+    dict(archive=_cache(n_slots=40, dtype=sc.SEGC_BF16, k_scale=None, v_scale=None)),   # dtype differs
+    dict(archive=_cache(n_slots=40, n_heads=8)), dict(archive=_cache(n_slots=40, tokens_per_frame=100)),
+    dict(n=-1),
+    dict(af=(0, 40)), dict(af=(-1, 0)), dict(slots=(2, 8)), dict(slots=(3, 3)),   # range, duplicate
+    dict(af=(0, 1), slots=(2, 3)),      # stand-in pointers are neither pinned host nor device memory
+])
+def test_archive_rejects(kw):
+    assert _fetch(**kw) == sc.SEGC_EINVAL
+    assert lib.segcausal_last_error().decode()
+
+
+def test_archive_store_checks_and_noop():
+    a, c = _cache(n_slots=40), _cache()
+    assert lib.kv_archive_store(ctypes.byref(c), _frames(9), ctypes.byref(a), _frames(0), 1, None) == 1
+    assert lib.kv_archive_store(ctypes.byref(c), _frames(1, 2), ctypes.byref(a), _frames(5, 5), 2, None) == 1
+    assert lib.kv_archive_store(ctypes.byref(c), None, ctypes.byref(a), None, 0, None) == 0
+    assert _fetch(af=(), slots=(), n=0) == 0
+    with pytest.raises(ValueError):
+        sc.kv_archive_fetch(sc.KVCache.__new__(sc.KVCache), [0, 1], None, [0])

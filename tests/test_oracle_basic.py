@@ -262,3 +262,27 @@ def test_dequant_bf16_closed_forms():
     assert np.array_equal(d, -oracle.dequantise_int8_bf16((-codes.astype(np.int16)).astype(np.int8), s))
     exact = oracle.dequantise_int8(codes, s)
     assert np.all(np.abs(d - exact) <= np.abs(exact) * (2.0 ** -8 + 2.0 ** -24))
+
+
+# ------------------------------------------------------------ archive ----
+
+def test_move_frames_matches_elementwise_loop():
+    rng = np.random.default_rng(31)
+    src = rng.integers(-127, 128, size=(9, 2, 3, 4)).astype(np.int8)
+    dst = rng.integers(-127, 128, size=(6, 2, 3, 4)).astype(np.int8)
+    src_idx, dst_idx = [8, 0, 3, 4], [5, 1, 2, 3]
+    got = oracle.move_frames(src, src_idx, dst, dst_idx)
+    want = dst.copy()
+    for s_, d_ in zip(src_idx, dst_idx):
+        for idx in np.ndindex(*src.shape[1:]):
+            want[(d_,) + idx] = src[(s_,) + idx]
+    assert np.array_equal(got, want)
+    assert np.array_equal(dst[[0, 4]], got[[0, 4]])          # untouched frames
+    back = oracle.move_frames(got, dst_idx, np.zeros_like(src), src_idx)
+    assert np.array_equal(back[src_idx], src[src_idx])       # round trip
+
+
+def test_move_frames_rejects_duplicate_destinations():
+    a = np.zeros((4, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.move_frames(a, [0, 1], a, [2, 2])
