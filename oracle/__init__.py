@@ -23,7 +23,8 @@ describing Hy-Nomas:
 * The Explainer's section "The training recipe" (segment forcing on packed
   sequences) for the gradients of the packed form (attention_bwd.py).
 * The model card's "Single-GPU Low-Memory Inference" for the CPU history
-  archive (archive.py).
+  archive (archive.py) and, with its assets table, for the INT8-weight
+  linear layer (linear.py).
 
 Readings where the pages leave a step open are listed in each module.
 
@@ -39,6 +40,7 @@ from .quant import quantise_int8, dequantise_int8, dequantise_int8_bf16
 from .window import window_select, WindowError
 from .attention_bwd import joint_attn_backward, joint_attn_dq_rows
 from .archive import move_frames
+from .linear import w8a16_linear
 from .attention import (Segment, visible_mask, history_keys, joint_attn,
                         joint_attn_rows)
 
@@ -49,4 +51,5 @@ __all__ = [
     "window_select", "WindowError",
     "Segment", "visible_mask", "history_keys", "joint_attn", "joint_attn_rows",
     "dequantise_int8_bf16", "joint_attn_backward", "joint_attn_dq_rows", "move_frames",
+    "w8a16_linear",
 ]

@@ -286,3 +286,37 @@ def test_move_frames_rejects_duplicate_destinations():
     a = np.zeros((4, 2), np.float32)
     with pytest.raises(ValueError):
         oracle.move_frames(a, [0, 1], a, [2, 2])
+
+
+# -------------------------------------------------------- W8A16 linear ----
+
+def test_w8a16_linear_matches_triple_loop():
+    rng = np.random.default_rng(41)
+    m, n, k = 3, 5, 7
+    x = rng.standard_normal((m, k))
+    codes = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
+    scale = rng.random(n) / 64
+    bias = rng.standard_normal(n)
+    got = oracle.w8a16_linear(x, codes, scale, bias)
+    for i in range(m):
+        for j in range(n):
+            acc = 0.0
+            for t in range(k):
+                acc += x[i, t] * (int(codes[j, t]) * scale[j])
+            assert abs(got[i, j] - (acc + bias[j])) <= 1e-12 * (1 + abs(acc))
+
+
+def test_w8a16_linear_special_cases():
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((4, 6))
+    # one-hot codes pick a column of x, scaled
+    codes = np.zeros((3, 6), np.int8)
+    codes[0, 2], codes[1, 5], codes[2, 0] = 1, -127, 64
+    scale = np.array([0.5, 2.0 ** -7, 0.25])
+    y = oracle.w8a16_linear(x, codes, scale)
+    assert np.array_equal(y[:, 0], 0.5 * x[:, 2])
+    assert np.array_equal(y[:, 1], -127 * 2.0 ** -7 * x[:, 5])
+    assert np.array_equal(y[:, 2], 16.0 * x[:, 0])
+    # no bias equals zero bias; a bias shifts every row
+    assert np.array_equal(y, oracle.w8a16_linear(x, codes, scale, np.zeros(3)))
+    assert np.allclose(oracle.w8a16_linear(x, codes, scale, [1, 2, 3]) - y, [[1, 2, 3]] * 4, atol=0)
