@@ -12,6 +12,8 @@ timed region. Prints one JSON line.
       forward + backward of one layer's attention over 346,528 packed rows)
   python bench.py --archive [--steps K] [--warmup W] (CPU history archive:
       window fetch and segment store over PCIe, overlap with attention)
+  python bench.py --linear [--steps K] [--warmup W]  (INT8-weight linears of
+      one block's video stream at 63,360 rows)
 """
 
 import argparse
@@ -453,6 +455,105 @@ def archive_bench(args):
     print(json.dumps(line), flush=True)
 
 
+LINEAR_METRIC = "INT8-weight linear TFLOP/s over one block's video-stream linears (QKV, proj, MLP up, down)"
+
+
+def linear_bench(args):
+    """W8A16 linears of one double-stream block's video stream at c4's
+    63,360 rows: QKV 2048 -> 6144, projection 2048 -> 2048, MLP 2048 -> 8192
+    and 8192 -> 2048; one step = the four calls (code expansion + product)."""
+    import torch
+    import segment_causal_dit_amd as sc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops = []
+    for name, (m, n, k) in workloads.LINEARS.items():
+        log("generating %s inputs" % name)
+        x, codes, scale, bias = workloads.linear_inputs(m, n, k)
+        ops.append(dict(name=name, m=m, n=n, k=k,
+                        x=torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev),
+                        w=torch.from_numpy(codes).to(dev), s=torch.from_numpy(scale).to(dev),
+                        b=torch.from_numpy(bias).to(dev),
+                        y=torch.empty((m, n), dtype=torch.bfloat16, device=dev),
+                        ws=torch.empty(n * k, dtype=torch.bfloat16, device=dev), ev=[]))
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        for o in ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sc.w8a16_linear(o["x"], o["w"], o["s"], o["b"], out=o["y"], workspace=o["ws"])
+            b.record(stream)
+            o["ev"].append((a, b))
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    for o in ops:
+        o["ev"].clear()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    total_flops = sum(2 * o["m"] * o["n"] * o["k"] for o in ops)
+    per = {}
+    for o in ops:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in o["ev"]]))
+        tf = 2 * o["m"] * o["n"] * o["k"] / (ms * 1e-3) / 1e12
+        per[o["name"]] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log("%-8s m=%d n=%d k=%d  %.3f ms  %.1f TFLOP/s (%.1f%% of bf16 peak)"
+            % (o["name"], o["m"], o["n"], o["k"], ms, tf, 100 * tf / PEAK_BF16_TFLOPS))
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    qkv = per["qkv"]
+    line = {
+        "metric": LINEAR_METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "linears: the video stream of one double-stream block at 63,360 rows (c4's "
+                               "video tokens): QKV 2048->6144, proj 2048->2048, MLP 2048->8192, 8192->2048; "
+                               "INT8 codes + per-channel fp32 scales, bf16 activations, fp32 bias"},
+        "per_linear": per,
+        "roofline": {"bound": "mfma", "achieved": qkv["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": qkv["frac"], "traffic": None,
+                     "kernel": "QKV call (code expansion + product), 2 * 63,360 * 6,144 * 2,048 flops"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        del ops
+        torch.cuda.empty_cache()
+        dt, flops = 0.0, 0
+        for name, (m, n, k) in workloads.LINEARS.items():
+            x, codes, scale, bias = workloads.linear_inputs(m, n, k)
+            xs = oracle.bf16_bits_to_f64(x)
+            del x
+            t = time.perf_counter()
+            oracle.w8a16_linear(xs, codes, scale, bias)
+            dt += time.perf_counter() - t
+            flops += 2 * m * n * k
+            del xs
+        line["cpu_baseline"] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+                                "cores": os.cpu_count() or 1, "kind": "oracle",
+                                "sample": "all four linears at full size (numpy float64 matmul, %.1f s)" % dt}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -466,6 +567,8 @@ def main():
     ap.add_argument("--counters-workload", action="store_true",
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--linear", action="store_true",
+                    help="the INT8-weight linears of one block's video stream instead")
     ap.add_argument("--archive", action="store_true",
                     help="the CPU history archive instead: window fetch / segment store over PCIe, and "
                          "the fetch overlapped with an attention call")
@@ -490,6 +593,9 @@ def main():
         return
     if args.archive:
         archive_bench(args)
+        return
+    if args.linear:
+        linear_bench(args)
         return
 
     import torch

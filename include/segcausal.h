@@ -186,6 +186,37 @@ int kv_archive_store(const segc_cache* cache, const int32_t* slots, const segc_c
                      const int32_t* archive_frames, int32_t n, void* stream);
 
 /*
+ * w8a16_linear -- linear layer with INT8 weights and BF16 activations.
+ * Source: model card, assets table (the quantized distilled DiT stores
+ * weights in INT8, DiT linear computation stays BF16) and section
+ * "Single-GPU Low-Memory Inference"; Explainer, architecture notes (hidden
+ * size 2,048, feed-forward 8,192). This library's weight format: one fp32
+ * scale per output channel, weight value = code * scale, codes in
+ * [-127, 127].
+ *   y[i][j] = bf16( w_scale[j] * sum_t x[i][t] * w[j][t] + bias[j] )
+ * computed with bf16 MFMA products (codes are exact in bf16) and fp32
+ * accumulation; the scale and bias are applied in fp32, rounded once. The
+ * codes are first expanded to bf16 into `workspace` (one pass per call, on
+ * the same stream), which the product then reads.
+ *
+ * x       : bf16 [m][ldx] row-major, first k columns used
+ * w       : int8 [n][ldw] row-major codes, first k columns used
+ * w_scale : fp32 [n]; bias: fp32 [n] or NULL
+ * y       : bf16 [m][ldy] output, first n columns written
+ * workspace : caller-owned device memory of 2 * n * k bytes (bf16 [n][k]),
+ *           overwritten; it may not overlap x, w or y
+ * Errors: EINVAL on m outside [0, 2^31), negative n or k, ldx < k or not a
+ *   multiple of 8, ldw < k or not a multiple of 16, ldy < n or not a
+ *   multiple of 4, NULL or misaligned pointers (x, w, w_scale, bias,
+ *   workspace: 16 bytes; y: 8 bytes), y equal to x or w, a workspace
+ *   overlapping x, w or y; EUNSUPPORTED unless n is a multiple of 256 and k
+ *   a positive multiple of 64. m == 0 or n == 0 is a no-op.
+ */
+int w8a16_linear(const void* x, int64_t ldx, const int8_t* w, int64_t ldw, const float* w_scale,
+                 const float* bias, void* y, int64_t ldy, int64_t m, int32_t n, int32_t k, void* workspace,
+                 void* stream);
+
+/*
  * window_select -- choose the cached frames the attention reads (host only).
  * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
  * (a bounded set of historical latent frames, default budget 18, excluding
@@ -323,7 +354,7 @@ const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 3)
+#define SEGC_ABI_VERSION ((1 << 16) | 5)
 
 #ifdef __cplusplus
 }

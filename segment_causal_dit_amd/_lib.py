@@ -64,6 +64,7 @@ _lib.rope3d_apply.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp, _f64,
 _lib.kv_cache_append.argtypes = [ctypes.POINTER(SegcCache), _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
 _lib.kv_window_dequant.argtypes = [ctypes.POINTER(SegcCache), _vp, _i32, ctypes.POINTER(SegcCache), _vp]
 _lib.window_select.argtypes = [_pi32, _i32, _i32, _pi32, _pi32]
+_lib.w8a16_linear.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp]
 _lib.kv_archive_fetch.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.kv_archive_store.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
@@ -71,12 +72,13 @@ _lib.segcausal_joint_attn_bwd.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
 _lib.segcausal_last_error.restype = ctypes.c_char_p
 _lib.segcausal_abi_version.restype = ctypes.c_int
 for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store"):
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
+           "w8a16_linear"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
            "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
-           "segcausal_last_error", "segcausal_abi_version")
+           "w8a16_linear", "segcausal_last_error", "segcausal_abi_version")
 
 
 class SegcError(RuntimeError):
@@ -219,6 +221,38 @@ def kv_archive_store(cache, slots, archive, archive_frames, stream=None):
         raise ValueError("archive_frames and slots differ in length")
     _check(_lib.kv_archive_store(ctypes.byref(cache.desc), sl.ctypes.data_as(_pi32), ctypes.byref(archive.desc),
                                  af.ctypes.data_as(_pi32), len(af), _stream(stream)))
+
+
+def w8a16_linear(x, w_codes, w_scale, bias=None, out=None, workspace=None, stream=None):
+    """y = bf16(x @ (w_codes * w_scale[:, None]).T + bias).
+
+    x : bf16 [m, k] (row stride a multiple of 8, unit column stride)
+    w_codes : int8 [n, k]; w_scale, bias : fp32 [n]; out : optional bf16 [m, n]
+    workspace : optional bf16 tensor of >= n * k elements (the expanded codes)
+    """
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 [m, k] with contiguous rows")
+    if w_codes.dtype != torch.int8 or w_codes.dim() != 2 or w_codes.stride(1) != 1:
+        raise ValueError("w_codes must be int8 [n, k] with contiguous rows")
+    m, k = x.shape
+    n = w_codes.shape[0]
+    if w_codes.shape[1] != k:
+        raise ValueError("w_codes must have k = %d columns" % k)
+    for name, t in (("w_scale", w_scale), ("bias", bias)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n,) or not t.is_contiguous()):
+            raise ValueError("%s must be contiguous fp32 [n]" % name)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be bf16 [m, n] with contiguous rows")
+    if workspace is None:
+        workspace = torch.empty(n * k, dtype=torch.bfloat16, device=x.device)
+    if workspace.dtype != torch.bfloat16 or not workspace.is_contiguous() or workspace.numel() < n * k:
+        raise ValueError("workspace must be a contiguous bf16 tensor of >= n * k elements")
+    _check(_lib.w8a16_linear(x.data_ptr(), x.stride(0), w_codes.data_ptr(), w_codes.stride(0),
+                             w_scale.data_ptr(), bias.data_ptr() if bias is not None else None,
+                             out.data_ptr(), out.stride(0), m, n, k, workspace.data_ptr(), _stream(stream)))
+    return out
 
 
 def window_select(slot_t, budget):

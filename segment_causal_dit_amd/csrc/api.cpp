@@ -286,6 +286,53 @@ int kv_archive_store(const segc_cache* cache, const int32_t* slots, const segc_c
                      stream);
 }
 
+int w8a16_linear(const void* x, int64_t ldx, const int8_t* w, int64_t ldw, const float* w_scale,
+                 const float* bias, void* y, int64_t ldy, int64_t m, int32_t n, int32_t k, void* workspace,
+                 void* stream) {
+  if (m < 0 || m >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "m out of range");
+  if (n < 0 || k < 0) return fail(SEGC_EINVAL, "n and k must be >= 0");
+  if (n % 256 || k % 64 || k == 0)
+    return fail(SEGC_EUNSUPPORTED, "n must be a multiple of 256 and k a positive multiple of 64 (n=%d, k=%d)", n, k);
+  if (ldx < k || ldx % 8) return fail(SEGC_EINVAL, "ldx must be >= k and a multiple of 8");
+  if (ldw < k || ldw % 16) return fail(SEGC_EINVAL, "ldw must be >= k and a multiple of 16");
+  if (ldy < n || ldy % 4) return fail(SEGC_EINVAL, "ldy must be >= n and a multiple of 4");
+  if (m == 0 || n == 0) return ok();
+  if (!x || !w || !w_scale || !y || !workspace) return fail(SEGC_EINVAL, "NULL x/w/w_scale/y/workspace");
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & 7u) || !aligned16(w_scale) ||
+      (bias && !aligned16(bias)) || !aligned16(workspace))
+    return fail(SEGC_EINVAL, "x, w, w_scale, bias, workspace must be 16-byte and y 8-byte aligned");
+  if ((int64_t)n * k >= ((int64_t)1 << 36)) return fail(SEGC_EINVAL, "weights too large");
+  {
+    // the workspace is written while x, w, y are in use: it may overlap none of them
+    const uintptr_t ws = (uintptr_t)workspace, we = ws + (uintptr_t)(2 * (int64_t)n * k);
+    const uintptr_t spans[3][2] = {
+        {(uintptr_t)x, (uintptr_t)x + (uintptr_t)(2 * ((m - 1) * ldx + k))},
+        {(uintptr_t)w, (uintptr_t)w + (uintptr_t)((int64_t)(n - 1) * ldw + k)},
+        {(uintptr_t)y, (uintptr_t)y + (uintptr_t)(2 * ((m - 1) * ldy + n))}};
+    for (int i = 0; i < 3; ++i)
+      if (ws < spans[i][1] && spans[i][0] < we) return fail(SEGC_EINVAL, "workspace overlaps x, w or y");
+  }
+  const int64_t tiles = ((m + 255) / 256) * (int64_t)(n / 256);
+  if (tiles >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "problem too large");
+  if ((const void*)y == x || (const void*)y == (const void*)w)
+    return fail(SEGC_EINVAL, "y must not be x or w (in place)");
+  segc::W8GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = (const uint16_t*)x;
+  p.w = w;
+  p.scale = w_scale;
+  p.bias = bias;
+  p.y = (uint16_t*)y;
+  p.wbf = (uint16_t*)workspace;
+  p.ldx = ldx;
+  p.ldw = ldw;
+  p.ldy = ldy;
+  p.M = (int32_t)m;
+  p.N = n;
+  p.K = k;
+  return hip_status(segc::launch_w8a16(p, (hipStream_t)stream), "w8a16_linear launch");
+}
+
 int window_select(const int32_t* slot_t, int32_t n_slots, int32_t budget, int32_t* out_slots,
                   int32_t* out_n) {
   if (n_slots < 0) return fail(SEGC_EINVAL, "n_slots < 0");

@@ -114,4 +114,18 @@ struct AttnBwdParams {
 };
 hipError_t launch_attn_bwd(const AttnBwdParams& p, hipStream_t s);
 
+// Linear with INT8 weights: y[M][N] = bf16(scale[n] * x[M][K] . code[n][K] + bias[n]).
+struct W8GemmParams {
+  const uint16_t* x;         // bf16 [M][ldx]
+  const int8_t* w;           // int8 [N][ldw]
+  const float* scale;        // [N]
+  const float* bias;         // [N] or null
+  uint16_t* y;               // bf16 [M][ldy]
+  uint16_t* wbf;             // workspace: the codes as bf16, dense [N][K]
+  int64_t ldx, ldw, ldy;     // elements
+  int32_t M, N, K;
+  int32_t n_tiles, m_tiles;  // set by the launcher
+};
+hipError_t launch_w8a16(const W8GemmParams& p, hipStream_t s);
+
 }  // namespace segc

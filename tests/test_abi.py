@@ -297,3 +297,33 @@ def test_archive_store_checks_and_noop():
     assert _fetch(af=(), slots=(), n=0) == 0
     with pytest.raises(ValueError):
         sc.kv_archive_fetch(sc.KVCache.__new__(sc.KVCache), [0, 1], None, [0])
+
+
+# -------------------------------------------------------- W8A16 linear ----
+
+def _lin(**kw):
+    a = dict(x=FAKE, ldx=2048, w=FAKE, ldw=2048, s=FAKE, b=None, y=FAKE2, ldy=6144, m=100, n=6144, k=2048,
+             ws=FAKE2 + 0x4000000)
+    a.update(kw)
+    return lib.w8a16_linear(a["x"], a["ldx"], a["w"], a["ldw"], a["s"], a["b"], a["y"], a["ldy"], a["m"],
+                            a["n"], a["k"], a["ws"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=-1), 1), (dict(m=1 << 31), 1), (dict(n=-256), 1), (dict(k=-64), 1),
+    (dict(n=300), 2), (dict(k=100), 2), (dict(k=0), 2),
+    (dict(ldx=2040), 1), (dict(ldx=2052), 1), (dict(ldw=2056), 1), (dict(ldy=6146), 1), (dict(ldy=100), 1),
+    (dict(x=None), 1), (dict(w=None), 1), (dict(s=None), 1), (dict(y=None), 1),
+    (dict(x=FAKE + 8), 1), (dict(s=FAKE + 4), 1), (dict(b=FAKE + 4), 1), (dict(y=FAKE2 + 4), 1),
+    (dict(y=FAKE), 1),                                   # in place over x
+    (dict(ws=None), 1), (dict(ws=FAKE2 + 0x4000000 + 8), 1),
+    (dict(ws=FAKE2 + 4096), 1),                          # workspace overlaps y
+])
+def test_w8a16_rejects(kw, code):
+    assert _lin(**kw) == code
+    assert lib.segcausal_last_error().decode()
+
+
+def test_w8a16_noop():
+    assert _lin(m=0, x=None, w=None, s=None, y=None) == 0
+    assert _lin(n=0, ldy=0, x=None, w=None, s=None, y=None) == 0

@@ -258,6 +258,34 @@ def upstream_grad(cfg):
     return normal_bf16(7, (cfg.n_cur, cfg.n_heads, HEAD_DIM))
 
 
+# Linear layers of one double-stream block's video stream at c4's 63,360
+# video rows (Explainer, architecture notes: hidden 2,048, feed-forward
+# 8,192; model card: INT8 DiT weights with BF16 linear compute):
+# (rows m, output channels n, input features k).
+LINEARS = {
+    "qkv": (63360, 3 * 2048, 2048),
+    "proj": (63360, 2048, 2048),
+    "mlp_up": (63360, 8192, 2048),
+    "mlp_down": (63360, 2048, 8192),
+}
+
+
+def linear_inputs(m, n, k, seed=0):
+    """Seeded W8A16 linear inputs: x bf16 bits [m, k] ~ N(0, 1); codes int8
+    [n, k] = round(48 N(0, 1)) clipped to [-127, 127]; per-channel scales fp32
+    [n] uniform in [1, 2) / (64 sqrt(k)) (outputs of order one); bias fp32 [n]
+    ~ N(0, 1). Draws from PCG64(42 + 8 + seed)."""
+    rng = np.random.Generator(np.random.PCG64(SEED + 8 + seed))
+    x = np.empty((m, k), dtype=np.uint16)
+    for a in range(0, m, max(1, _CHUNK // k)):
+        b = min(m, a + max(1, _CHUNK // k))
+        x[a:b] = f32_to_bf16_bits(rng.standard_normal((b - a, k), dtype=np.float32))
+    codes = np.clip(np.rint(rng.standard_normal((n, k), dtype=np.float32) * 48.0), -127, 127).astype(np.int8)
+    scale = ((1.0 + rng.random(n)) / (64.0 * math.sqrt(k))).astype(np.float32)
+    bias = rng.standard_normal(n).astype(np.float32)
+    return x, codes, scale, bias
+
+
 def direct_int8_cache(cfg, frames):
     """Seeded INT8 codes and fp32 scales for `frames` cache slots, drawn
     directly (for attention-only checks on identical cache bytes).
