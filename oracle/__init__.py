@@ -25,6 +25,8 @@ describing Hy-Nomas:
 * The model card's "Single-GPU Low-Memory Inference" for the CPU history
   archive (archive.py) and, with its assets table, for the INT8-weight
   linear layer (linear.py).
+* The model card's "Text and Camera Conditioning" for the per-latent-frame
+  camera cross-attention (camera.py).
 
 Readings where the pages leave a step open are listed in each module.
 
@@ -41,6 +43,7 @@ from .window import window_select, WindowError
 from .attention_bwd import joint_attn_backward, joint_attn_dq_rows
 from .archive import move_frames
 from .linear import w8a16_linear
+from .camera import camera_cross_attn
 from .attention import (Segment, visible_mask, history_keys, joint_attn,
                         joint_attn_rows)
 
@@ -51,5 +54,5 @@ __all__ = [
     "window_select", "WindowError",
     "Segment", "visible_mask", "history_keys", "joint_attn", "joint_attn_rows",
     "dequantise_int8_bf16", "joint_attn_backward", "joint_attn_dq_rows", "move_frames",
-    "w8a16_linear",
+    "w8a16_linear", "camera_cross_attn",
 ]

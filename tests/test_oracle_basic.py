@@ -320,3 +320,40 @@ def test_w8a16_linear_special_cases():
     # no bias equals zero bias; a bias shifts every row
     assert np.array_equal(y, oracle.w8a16_linear(x, codes, scale, np.zeros(3)))
     assert np.allclose(oracle.w8a16_linear(x, codes, scale, [1, 2, 3]) - y, [[1, 2, 3]] * 4, atol=0)
+
+
+# ------------------------------------------------ camera cross-attention ----
+
+def test_camera_cross_attn_matches_loops():
+    rng = np.random.default_rng(51)
+    n, h, d, tpc, tc = 11, 2, 5, 4, 3            # a ragged last chunk of 3 rows
+    q = rng.standard_normal((n, h, d))
+    nch = (n + tpc - 1) // tpc
+    k = rng.standard_normal((nch * tc, h, d))
+    v = rng.standard_normal((nch * tc, h, d))
+    got = oracle.camera_cross_attn(q, k, v, tpc, tc, 0.7)
+    for i in range(n):
+        c = i // tpc
+        for hd in range(h):
+            s = [0.7 * sum(q[i, hd, t] * k[c * tc + j, hd, t] for t in range(d)) for j in range(tc)]
+            e = [math.exp(x - max(s)) for x in s]
+            for t in range(d):
+                want = sum(e[j] * v[c * tc + j, hd, t] for j in range(tc)) / sum(e)
+                assert abs(got[i, hd, t] - want) <= 1e-12
+
+
+def test_camera_cross_attn_closed_forms():
+    rng = np.random.default_rng(52)
+    n, h, d, tpc = 10, 3, 4, 5
+    q = rng.standard_normal((n, h, d)) * 10
+    v = rng.standard_normal((2, h, d))
+    # one camera token per chunk: every row gets its chunk's value exactly
+    o = oracle.camera_cross_attn(q, rng.standard_normal((2, h, d)), v, tpc, 1, 0.088)
+    assert np.array_equal(o[:5], np.broadcast_to(v[0], (5, h, d)))
+    assert np.array_equal(o[5:], np.broadcast_to(v[1], (5, h, d)))
+    # identical keys: the plain mean of the chunk's values
+    k = np.broadcast_to(rng.standard_normal((1, h, d)), (6, h, d))
+    v3 = rng.standard_normal((6, h, d))
+    o = oracle.camera_cross_attn(q, k, v3, tpc, 3, 0.5)
+    assert np.allclose(o[:5], v3[:3].mean(axis=0), atol=1e-14)
+    assert np.allclose(o[5:], v3[3:].mean(axis=0), atol=1e-14)
