@@ -14,6 +14,8 @@ timed region. Prints one JSON line.
       window fetch and segment store over PCIe, overlap with attention)
   python bench.py --linear [--steps K] [--warmup W]  (INT8-weight linears of
       one block's video stream at 63,360 rows)
+  python bench.py --camera [--steps K] [--warmup W]  (camera cross-attention
+      of c4's video rows)
 """
 
 import argparse
@@ -554,6 +556,87 @@ def linear_bench(args):
     print(json.dumps(line), flush=True)
 
 
+CAMERA_METRIC = "camera cross-attention GB/s (video rows x heads over their latent frame's camera tokens)"
+
+
+def camera_bench(args):
+    """Camera cross-attention over c4's 63,360 video rows (72 latent frames of
+    880 tokens, 16 heads): one camera token per latent frame (the pages'
+    configuration: o = v of the frame, a pure write), and four tokens per frame
+    through the general softmax path."""
+    import torch
+    import segment_causal_dit_amd as sc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.CONFIGS["c4"]
+    n, h, tpc = cfg.n_video, cfg.n_heads, cfg.tokens_per_frame
+    n_frames = n // tpc
+    q = torch.from_numpy(workloads.normal_bf16(20, (n, h, HEAD_DIM)).view(np.int16)).view(torch.bfloat16).to(dev)
+    res = {}
+    for t_cam in (1, 4):
+        k = torch.from_numpy(workloads.normal_bf16(21, (n_frames * t_cam, h, HEAD_DIM)).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        v = torch.from_numpy(workloads.normal_bf16(22, (n_frames * t_cam, h, HEAD_DIM)).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        o = torch.empty_like(q)
+        for _ in range(args.warmup):
+            sc.camera_cross_attn(q, k, v, tpc, 1.0 / math.sqrt(HEAD_DIM), out=o)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            sc.camera_cross_attn(q, k, v, tpc, 1.0 / math.sqrt(HEAD_DIM), out=o)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        byts = n * h * HEAD_DIM * 2 * (1 if t_cam == 1 else 2)      # o written (and q read)
+        res[t_cam] = (ms, byts / (ms * 1e-3) / 1e9)
+        log("t_cam %d: %.4f ms  %.0f GB/s (%.1f%% of HBM peak)" % (t_cam, ms, res[t_cam][1],
+                                                                  100 * res[t_cam][1] / PEAK_HBM_GBS))
+    ms1, gbs1 = res[1]
+    line = {
+        "metric": CAMERA_METRIC,
+        "value": round(gbs1, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms1, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "camera: c4's 63,360 video rows (72 latent frames of 22x40) x 16 heads x 128, "
+                               "one camera token per latent frame (o = v of the frame, 259.5 MB written); "
+                               "four tokens per frame through the softmax path reported beside it"},
+        "general_path_t_cam4": {"ms": round(res[4][0], 4), "gbs": round(res[4][1], 1),
+                                "hbm_frac": round(res[4][1] / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs1, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs1 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "camera_attn_kernel, one camera token per frame: 256 B written per (row, head)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        f = oracle.bf16_bits_to_f64
+        rows = n                              # all 72 latent frames, four camera tokens each
+        qs = f(workloads.normal_bf16(20, (n, h, HEAD_DIM)))
+        ks = f(workloads.normal_bf16(21, (n_frames * 4, h, HEAD_DIM)))
+        vs = f(workloads.normal_bf16(22, (n_frames * 4, h, HEAD_DIM)))
+        t = time.perf_counter()
+        oracle.camera_cross_attn(qs, ks, vs, tpc, 4, 1.0 / math.sqrt(HEAD_DIM))
+        dt = time.perf_counter() - t
+        line["cpu_baseline"] = {"value": round(rows * h * HEAD_DIM * 2 * 2 / dt / 1e9, 3), "unit": "GB/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": "the oracle's softmax path on all 72 latent frames (63,360 rows x 16 "
+                                          "heads, 4 camera tokens each; numpy float64, %.1f s)" % dt}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -567,6 +650,8 @@ def main():
     ap.add_argument("--counters-workload", action="store_true",
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--camera", action="store_true",
+                    help="the per-latent-frame camera cross-attention instead")
     ap.add_argument("--linear", action="store_true",
                     help="the INT8-weight linears of one block's video stream instead")
     ap.add_argument("--archive", action="store_true",
@@ -596,6 +681,9 @@ def main():
         return
     if args.linear:
         linear_bench(args)
+        return
+    if args.camera:
+        camera_bench(args)
         return
 
     import torch

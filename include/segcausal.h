@@ -217,6 +217,47 @@ int w8a16_linear(const void* x, int64_t ldx, const int8_t* w, int64_t ldw, const
                  void* stream);
 
 /*
+ * camera_cross_attn -- per-latent-frame camera cross-attention of the video
+ * rows.
+ * Source: model card, section "Text and Camera Conditioning" (camera
+ * extrinsics grouped over four video frames into one 64-dimensional input
+ * per latent frame; at every double-stream block the video tokens query the
+ * projected camera features through cross-attention after the video MLP;
+ * per-chunk camera attention with a chunk size of one latent frame).
+ *
+ * Row r (0 <= r < n_tok) belongs to chunk c = r / tokens_per_chunk (e.g.
+ * tokens_per_chunk = 880 for one 22x40 latent frame) and attends to camera
+ * rows c*t_cam .. c*t_cam + t_cam - 1 of k and v. Per head:
+ *   o_r = sum_j softmax_j(sm_scale * q_r . k_j) v_j
+ * in fp32 from bf16 inputs, rounded once to bf16. With t_cam == 1 (the pages'
+ * configuration, one camera token per latent frame) the weight is exactly 1
+ * and o_r = v of the chunk; q is then not read and may be NULL.
+ */
+typedef struct segc_camera_args {
+  const void* q;   /* bf16 [n_tok] rows (video queries) */
+  const void* k;   /* bf16 [ceil(n_tok / tokens_per_chunk) * t_cam] rows (camera keys) */
+  const void* v;   /* bf16, same rows and strides as k (camera values) */
+  void*       o;   /* bf16 [n_tok] rows, output */
+  int64_t q_stride_tok, q_stride_head;
+  int64_t kv_stride_tok, kv_stride_head;
+  int64_t o_stride_tok, o_stride_head;
+  int64_t n_tok;
+  int32_t n_heads;
+  int32_t head_dim;          /* must be 128 */
+  int32_t tokens_per_chunk;  /* >= 1 */
+  int32_t t_cam;             /* camera tokens per chunk, 1 .. 4096 */
+  float   sm_scale;          /* > 0 */
+} segc_camera_args;
+
+/*
+ * Errors: EINVAL on null/misaligned pointers (q only when t_cam > 1), n_tok
+ *   outside [0, 2^31), n_heads outside [1, 1024], tokens_per_chunk < 1, t_cam
+ *   outside [1, 4096], bad strides, sm_scale <= 0 or not finite, o equal to
+ *   q, k or v; EUNSUPPORTED if head_dim != 128. n_tok == 0 is a no-op.
+ */
+int camera_cross_attn(const segc_camera_args* args, void* stream);
+
+/*
  * window_select -- choose the cached frames the attention reads (host only).
  * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
  * (a bounded set of historical latent frames, default budget 18, excluding
@@ -354,7 +395,7 @@ const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 5)
+#define SEGC_ABI_VERSION ((1 << 16) | 6)
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,7 @@ fallback implementation.
 
 _NAMES = (
     "SEGC_OK", "SEGC_EINVAL", "SEGC_EUNSUPPORTED", "SEGC_EHIP", "SEGC_BF16", "SEGC_INT8",
-    "KVCache", "SegcError", "abi_version", "kv_archive_fetch", "kv_archive_store", "kv_cache_append",
+    "KVCache", "SegcError", "abi_version", "camera_cross_attn", "kv_archive_fetch", "kv_archive_store", "kv_cache_append",
     "kv_window_dequant", "rope3d_apply",
     "segcausal_joint_attn", "segcausal_joint_attn_bwd", "w8a16_linear", "window_select", "LIB_PATH",
     "EXPORTS",

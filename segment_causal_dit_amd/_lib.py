@@ -60,11 +60,21 @@ class SegcAttnBwdArgs(ctypes.Structure):
                 ("sm_scale", _f32)]
 
 
+class SegcCameraArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("o", _vp),
+                ("q_stride_tok", _i64), ("q_stride_head", _i64),
+                ("kv_stride_tok", _i64), ("kv_stride_head", _i64),
+                ("o_stride_tok", _i64), ("o_stride_head", _i64),
+                ("n_tok", _i64), ("n_heads", _i32), ("head_dim", _i32),
+                ("tokens_per_chunk", _i32), ("t_cam", _i32), ("sm_scale", _f32)]
+
+
 _lib.rope3d_apply.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _i64, _vp, _f64, _i32, _i32, _i32, _vp]
 _lib.kv_cache_append.argtypes = [ctypes.POINTER(SegcCache), _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp]
 _lib.kv_window_dequant.argtypes = [ctypes.POINTER(SegcCache), _vp, _i32, ctypes.POINTER(SegcCache), _vp]
 _lib.window_select.argtypes = [_pi32, _i32, _i32, _pi32, _pi32]
 _lib.w8a16_linear.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp]
+_lib.camera_cross_attn.argtypes = [ctypes.POINTER(SegcCameraArgs), _vp]
 _lib.kv_archive_fetch.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.kv_archive_store.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
@@ -73,12 +83,12 @@ _lib.segcausal_last_error.restype = ctypes.c_char_p
 _lib.segcausal_abi_version.restype = ctypes.c_int
 for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
            "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
-           "w8a16_linear"):
+           "w8a16_linear", "camera_cross_attn"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
            "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
-           "w8a16_linear", "segcausal_last_error", "segcausal_abi_version")
+           "w8a16_linear", "camera_cross_attn", "segcausal_last_error", "segcausal_abi_version")
 
 
 class SegcError(RuntimeError):
@@ -252,6 +262,28 @@ def w8a16_linear(x, w_codes, w_scale, bias=None, out=None, workspace=None, strea
     _check(_lib.w8a16_linear(x.data_ptr(), x.stride(0), w_codes.data_ptr(), w_codes.stride(0),
                              w_scale.data_ptr(), bias.data_ptr() if bias is not None else None,
                              out.data_ptr(), out.stride(0), m, n, k, workspace.data_ptr(), _stream(stream)))
+    return out
+
+
+def camera_cross_attn(q, k_cam, v_cam, tokens_per_chunk, sm_scale, out=None, stream=None):
+    """Each row of q [n, H, 128] attends to the camera rows of its chunk:
+    k_cam, v_cam [n_chunks * t_cam, H, 128] with t_cam = rows / n_chunks."""
+    n, nh = q.shape[0], q.shape[1]
+    n_chunks = (n + tokens_per_chunk - 1) // tokens_per_chunk
+    if n_chunks == 0 or k_cam.shape[0] % n_chunks:
+        raise ValueError("camera rows must be a whole number per chunk")
+    t_cam = k_cam.shape[0] // n_chunks
+    if k_cam.shape != v_cam.shape or k_cam.stride() != v_cam.stride():
+        raise ValueError("k_cam and v_cam must share shape and strides")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    pq, qst, qsh = _rows(q, "q")
+    pk, kst, ksh = _rows(k_cam, "k_cam")
+    pv, _, _ = _rows(v_cam, "v_cam")
+    po, ost, osh = _rows(out, "out")
+    args = SegcCameraArgs(pq, pk, pv, po, qst, qsh, kst, ksh, ost, osh, n, nh, HEAD_DIM,
+                          int(tokens_per_chunk), t_cam, float(sm_scale))
+    _check(_lib.camera_cross_attn(ctypes.byref(args), _stream(stream)))
     return out
 
 

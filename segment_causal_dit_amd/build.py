@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsegcausal.so")
-SOURCES = ["api.cpp", "rope.hip", "append.hip", "dequant.hip", "attn.hip", "attn_bwd.hip", "gemm_w8.hip"]
+SOURCES = ["api.cpp", "rope.hip", "append.hip", "dequant.hip", "attn.hip", "attn_bwd.hip", "gemm_w8.hip", "camera.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -333,6 +333,43 @@ int w8a16_linear(const void* x, int64_t ldx, const int8_t* w, int64_t ldw, const
   return hip_status(segc::launch_w8a16(p, (hipStream_t)stream), "w8a16_linear launch");
 }
 
+int camera_cross_attn(const segc_camera_args* a, void* stream) {
+  if (!a) return fail(SEGC_EINVAL, "args is NULL");
+  if (a->head_dim != SEGC_HEAD_DIM) return fail(SEGC_EUNSUPPORTED, "head_dim %d != 128", a->head_dim);
+  if (a->n_tok < 0 || a->n_tok >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "n_tok out of range");
+  if (a->n_heads < 1 || a->n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  if (a->tokens_per_chunk < 1) return fail(SEGC_EINVAL, "tokens_per_chunk must be >= 1");
+  if (a->t_cam < 1 || a->t_cam > 4096) return fail(SEGC_EINVAL, "t_cam must be in [1, 4096]");
+  if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
+    return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
+  if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->kv_stride_tok, a->kv_stride_head) ||
+      !strides_ok(a->o_stride_tok, a->o_stride_head))
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+  if (a->n_tok == 0) return ok();
+  if (!a->k || !a->v || !a->o || (a->t_cam > 1 && !a->q)) return fail(SEGC_EINVAL, "NULL q/k/v/o");
+  if ((a->q && !aligned16(a->q)) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(SEGC_EINVAL, "q/k/v/o must be 16-byte aligned");
+  if (a->o == a->q || a->o == a->k || a->o == a->v) return fail(SEGC_EINVAL, "o must not be q, k or v (in place)");
+  segc::CamParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = (const uint16_t*)a->q;
+  p.k = (const uint16_t*)a->k;
+  p.v = (const uint16_t*)a->v;
+  p.o = (uint16_t*)a->o;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.kv_st = a->kv_stride_tok;
+  p.kv_sh = a->kv_stride_head;
+  p.o_st = a->o_stride_tok;
+  p.o_sh = a->o_stride_head;
+  p.n_tok = a->n_tok;
+  p.n_heads = a->n_heads;
+  p.tpc = a->tokens_per_chunk;
+  p.t_cam = a->t_cam;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  return hip_status(segc::launch_camera_attn(p, (hipStream_t)stream), "camera_cross_attn launch");
+}
+
 int window_select(const int32_t* slot_t, int32_t n_slots, int32_t budget, int32_t* out_slots,
                   int32_t* out_n) {
   if (n_slots < 0) return fail(SEGC_EINVAL, "n_slots < 0");

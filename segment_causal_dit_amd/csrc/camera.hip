@@ -1,0 +1,100 @@
+// Per-latent-frame camera cross-attention: each video row attends to the
+// camera tokens of its own chunk of latent frames.
+//
+// Source: "Hy-Nomas: Towards Free-Form Interactive World Generation" (model
+// card), section "Text and Camera Conditioning": camera extrinsics become one
+// 64-dimensional input per latent frame; at every double-stream block the
+// video tokens query the projected camera features through cross-attention
+// after the video MLP; with per-chunk camera attention and a chunk size of
+// one the attention is aligned to individual latent frames.
+//
+// Row r (of n_tok video rows) is in chunk c = r / tokens_per_chunk, whose
+// camera tokens are rows [c t_cam, (c + 1) t_cam) of k and v. Per head:
+//   o_r = sum_j softmax_j(sm_scale q_r . k_j) v_j.
+// 16 lanes take one (row, head): 16 bytes of q and o each, so a wave reads
+// and writes 1 KB contiguous when heads are contiguous. The chunk's camera
+// rows are shared by every row of the chunk and stay in the caches. With
+// one camera token per chunk (the pages' configuration) the softmax weight
+// is exactly 1 (exp2(s - s) = 1, l = 1), so o_r = v of the chunk: that case
+// skips q and the products and only writes (the same bits as the general
+// path for finite inputs).
+#include "internal.h"
+
+namespace segc {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ inline float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+constexpr int kThreads = 256;
+constexpr int kPairs = kThreads / 16;     // (row, head) pairs per workgroup
+
+__global__ __launch_bounds__(kThreads) void camera_attn_kernel(CamParams p) {
+  const int tid = threadIdx.x;
+  const int li = tid & 15;
+  const int64_t pair = (int64_t)blockIdx.x * kPairs + (tid >> 4);
+  const int64_t row = pair / p.n_heads;
+  const int head = (int)(pair - row * p.n_heads);
+  if (row >= p.n_tok) return;                 // whole 16-lane groups leave together
+  const int64_t chunk = row / p.tpc;
+  u32x4* dst = (u32x4*)(p.o + row * p.o_st + (int64_t)head * p.o_sh + 8 * li);
+  const int64_t cam0 = chunk * p.t_cam;
+  if (p.t_cam == 1) {
+    *dst = *(const u32x4*)(p.v + cam0 * p.kv_st + (int64_t)head * p.kv_sh + 8 * li);
+    return;
+  }
+  const u32x4 qv = *(const u32x4*)(p.q + row * p.q_st + (int64_t)head * p.q_sh + 8 * li);
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    qf[2 * e] = lo_f(qv[e]);
+    qf[2 * e + 1] = hi_f(qv[e]);
+  }
+  float m = -INFINITY, l = 0.0f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < p.t_cam; ++j) {
+    const int64_t off = (cam0 + j) * p.kv_st + (int64_t)head * p.kv_sh + 8 * li;
+    const u32x4 kv = *(const u32x4*)(p.k + off);
+    const u32x4 vv = *(const u32x4*)(p.v + off);
+    float d = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d = fmaf(qf[2 * e], lo_f(kv[e]), d);
+      d = fmaf(qf[2 * e + 1], hi_f(kv[e]), d);
+    }
+#pragma unroll
+    for (int s = 8; s >= 1; s >>= 1) d += __shfl_xor(d, s, 16);
+    const float sv = d * p.scale_log2;
+    const float mn = fmaxf(m, sv);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);       // 0 on the first key (m = -inf)
+    const float pr = __builtin_amdgcn_exp2f(sv - mn);
+    l = fmaf(l, alpha, pr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(acc[2 * e], alpha, pr * lo_f(vv[e]));
+      acc[2 * e + 1] = fmaf(acc[2 * e + 1], alpha, pr * hi_f(vv[e]));
+    }
+    m = mn;
+  }
+  const float inv = 1.0f / l;
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *dst = o;
+}
+
+}  // namespace
+
+hipError_t launch_camera_attn(const CamParams& p, hipStream_t s) {
+  const int64_t pairs = p.n_tok * p.n_heads;
+  hipLaunchKernelGGL(camera_attn_kernel, dim3((unsigned)((pairs + kPairs - 1) / kPairs)), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace segc

@@ -128,4 +128,18 @@ struct W8GemmParams {
 };
 hipError_t launch_w8a16(const W8GemmParams& p, hipStream_t s);
 
+// Camera cross-attention: row r attends to camera rows [c t_cam, (c+1) t_cam),
+// c = r / tpc.
+struct CamParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int64_t q_st, q_sh, kv_st, kv_sh, o_st, o_sh;   // elements
+  int64_t n_tok;
+  int32_t n_heads, tpc, t_cam;
+  float scale_log2;          // sm_scale * log2(e)
+};
+hipError_t launch_camera_attn(const CamParams& p, hipStream_t s);
+
 }  // namespace segc

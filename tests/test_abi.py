@@ -327,3 +327,29 @@ def test_w8a16_rejects(kw, code):
 def test_w8a16_noop():
     assert _lin(m=0, x=None, w=None, s=None, y=None) == 0
     assert _lin(n=0, ldy=0, x=None, w=None, s=None, y=None) == 0
+
+
+# ------------------------------------------------ camera cross-attention ----
+
+def _cam(**kw):
+    a = sc.SegcCameraArgs(FAKE, FAKE2, FAKE2 + 0x1000000, FAKE2 + 0x2000000, 2048, 128, 2048, 128, 2048, 128,
+                          1760, 16, 128, 880, 1, 0.088)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return lib.camera_cross_attn(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), 2), (dict(n_tok=-1), 1), (dict(n_tok=1 << 31), 1), (dict(n_heads=0), 1),
+    (dict(tokens_per_chunk=0), 1), (dict(t_cam=0), 1), (dict(t_cam=5000), 1), (dict(sm_scale=0.0), 1),
+    (dict(q_stride_tok=100), 1), (dict(kv_stride_head=-8), 1), (dict(k=None), 1), (dict(o=None), 1),
+    (dict(t_cam=2, q=None), 1), (dict(v=FAKE2 + 8), 1), (dict(o=FAKE2), 1),
+])
+def test_camera_rejects(kw, code):
+    assert _cam(**kw) == code
+    assert lib.segcausal_last_error().decode()
+
+
+def test_camera_noop():
+    assert _cam(n_tok=0, q=None, k=None, v=None, o=None) == 0
+    assert lib.camera_cross_attn(None, None) == 1

@@ -1,0 +1,102 @@
+"""GPU parity of the per-latent-frame camera cross-attention against the fp64
+oracle, through the C ABI.
+
+Bar (derived): logits are fp32 dot products of bf16 values (error far below
+2^-16 of |s| for 128 terms) and the output is a convex combination of the
+chunk's values accumulated in fp32 and rounded once to bf16, whose relative
+rounding error is at most 2^-8. Element-wise:
+    |o - o_ref| <= 2^-8 |o_ref| + 2^-16 max_j |v_j|.
+With one camera token per chunk the weight is exactly 1: o equals v bit for
+bit.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import HEAD_DIM
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+sc = pytest.importorskip("segment_causal_dit_amd._lib")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _bf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _inputs(n, h, tpc, t_cam, seed):
+    n_chunks = (n + tpc - 1) // tpc
+    q = workloads.normal_bf16(20 + seed, (n, h, HEAD_DIM))
+    k = workloads.normal_bf16(21 + seed, (n_chunks * t_cam, h, HEAD_DIM))
+    v = workloads.normal_bf16(22 + seed, (n_chunks * t_cam, h, HEAD_DIM))
+    return q, k, v
+
+
+def _check(got, want, v):
+    err = np.abs(got - want)
+    bound = 2.0 ** -8 * np.abs(want) + 2.0 ** -16 * np.abs(v).max()
+    _say("  max |err| %.3g, max err/bound %.3f" % (err.max(), (err / bound).max()))
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("n,h,tpc,t_cam", [
+    (2640, 4, 880, 4),      # three 22x40 frames, four camera tokens each
+    (1050, 2, 100, 3),      # ragged last chunk
+    (300, 3, 7, 16),        # many small chunks, more tokens than the chunk has rows
+])
+def test_general_path_matches_oracle(n, h, tpc, t_cam):
+    _say("camera", n, h, tpc, t_cam)
+    q, k, v = _inputs(n, h, tpc, t_cam, t_cam)
+    o = sc.camera_cross_attn(_bf(q), _bf(k), _bf(v), tpc, 1.0 / np.sqrt(HEAD_DIM))
+    torch.cuda.synchronize()
+    f = oracle.bf16_bits_to_f64
+    _check(_f64(o), oracle.camera_cross_attn(f(q), f(k), f(v), tpc, t_cam, 1.0 / np.sqrt(HEAD_DIM)), f(v))
+
+
+def test_one_token_per_frame_is_exact_at_c4_size():
+    # the pages' configuration at c4's 63,360 video rows: o is v of the row's frame, bit for bit
+    n, h, tpc = 63360, 16, 880
+    q, k, v = _inputs(n, h, tpc, 1, 0)
+    o = sc.camera_cross_attn(_bf(q), _bf(k), _bf(v), tpc, 1.0 / np.sqrt(HEAD_DIM))
+    torch.cuda.synchronize()
+    want = np.repeat(v, tpc, axis=0)
+    assert np.array_equal(_bits(o), want)
+
+
+def test_general_path_full_size_sampled_chunks_and_strides():
+    # four camera tokens per frame at c4's size; q and o as strided views; whole
+    # chunks (first, middle, last) against the oracle
+    n, h, tpc, t_cam = 63360, 16, 880, 4
+    q, k, v = _inputs(n, h, tpc, t_cam, 9)
+    qbuf = torch.zeros((n, 3, h, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    qbuf[:, 1] = _bf(q)
+    obuf = torch.zeros((n, 2, h, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    o = sc.camera_cross_attn(qbuf[:, 1], _bf(k), _bf(v), tpc, 1.0 / np.sqrt(HEAD_DIM), out=obuf[:, 0])
+    torch.cuda.synchronize()
+    assert not bool(obuf[:, 1].any())
+    f = oracle.bf16_bits_to_f64
+    for c in (0, 35, 71):
+        rows = slice(c * tpc, (c + 1) * tpc)
+        cam = slice(c * t_cam, (c + 1) * t_cam)
+        want = oracle.camera_cross_attn(f(q[rows]), f(k[cam]), f(v[cam]), tpc, t_cam, 1.0 / np.sqrt(HEAD_DIM))
+        _check(_f64(o[rows]), want, f(v[cam]))
