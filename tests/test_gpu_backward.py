@@ -174,3 +174,51 @@ def test_training_scale_sampled_rows_and_sums():
     dead = _invisible_keys(cfg)
     assert not bits(dk[torch.from_numpy(dead).cuda()]).any()
     assert not bits(dv[torch.from_numpy(dead).cuda()]).any()
+
+
+@pytest.mark.parametrize("n,h,segs", [
+    (1, 1, [(0, 0, 0)]),                         # one row: p = 1, dq = dk = 0, dv = do
+    (65, 2, [(0, 0, 0)]),                        # one row past a 64-row tile
+    (129, 1, [(0, 1, 1), (2, 0, 0), (3, 3, 2), (9, 0, 0)]),   # tiny segments, padded text
+    (300, 3, [(0, 300, 300)]),                   # all rows text
+])
+def test_edge_shapes(n, h, segs):
+    _say("bwd edge", n, h, segs)
+    q = workloads.normal_bf16(30, (n, h, 128), 1.0 / np.sqrt(128))
+    k, v, do = (workloads.normal_bf16(31 + i, (n, h, 128)) for i in range(3))
+    qt, kt, vt = _bf(q), _bf(k), _bf(v)
+    lse = torch.empty((h, n), dtype=torch.float32, device="cuda")
+    o = sc.segcausal_joint_attn(qt, kt, vt, segs, 1.0, lse=lse)
+    dq, dk, dv = sc.segcausal_joint_attn_bwd(qt, kt, vt, o, _bf(do), lse, segs, 1.0)
+    torch.cuda.synchronize()
+    f = oracle.bf16_bits_to_f64
+    osegs = [oracle.Segment(*s) for s in segs]
+    want = oracle.joint_attn_backward(f(q), f(k), f(v), osegs, f(do), sm_scale=1.0)
+    vis = oracle.visible_mask(0, osegs, n)                       # [query, key]
+    for nm, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        got = to_f64(g)
+        zero = np.sqrt(np.mean(w * w, axis=-1)) == 0             # [row, head]
+        # keys no query sees: p is exactly 0, so dk and dv are exactly 0
+        if nm != "dq":
+            unseen = ~vis.any(axis=0)
+            assert not got[unseen].any(), nm
+        # rows that are zero only by cancellation (a query seeing one key: ds =
+        # do.v - do.o with o = v): the kernel forms do.v and do.o in two fp32
+        # summation orders, so |ds| <= 2^-18 sum_t |do_t v_t| and
+        # |dq| <= |ds| max |k|
+        # (and dk_j = sm_scale sum_i ds_ij q_i likewise with |q|)
+        if nm in ("dq", "dk") and zero.any():
+            fq, fk, fv, fdo = f(q), f(k), f(v), f(do)
+            for r, hd in zip(*np.nonzero(zero)):
+                if nm == "dq":
+                    qs, ks_, other = np.array([r]), np.nonzero(vis[r])[0], fk
+                else:
+                    qs, ks_, other = np.nonzero(vis[:, r])[0], np.array([r]), fq
+                    if not len(qs):
+                        continue                          # unseen key: exact zero, checked above
+                terms = np.abs(fdo[qs, hd][:, None, :] * fv[ks_, hd][None, :, :]).sum(axis=-1).max()
+                big = np.abs(other[ks_ if nm == "dq" else qs, hd]).max()
+                bound = 2.0 ** -18 * terms * big
+                assert np.abs(got[r, hd]).max() <= bound, (nm, r, hd, np.abs(got[r, hd]).max(), bound)
+        if (~zero).any():
+            _check(nm, np.where(zero[..., None], w, got), w)
