@@ -13,7 +13,8 @@
 //   o_r = sum_j softmax_j(sm_scale q_r . k_j) v_j.
 // 16 lanes take one (row, head): 16 bytes of q and o each, so a wave reads
 // and writes 1 KB contiguous when heads are contiguous. The chunk's camera
-// rows are shared by every row of the chunk and stay in the caches. With
+// rows are shared by every row of the chunk and stay in the caches; keys are
+// taken four at a time so that their loads overlap. With
 // one camera token per chunk (the pages' configuration) the softmax weight
 // is exactly 1 (exp2(s - s) = 1, l = 1), so o_r = v of the chunk: that case
 // skips q and the products and only writes (the same bits as the general
@@ -32,6 +33,16 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 }
 __device__ inline float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Sum over the 16 lanes of a row with DPP (quad swaps, then the half-row and
+// row mirrors): every lane ends with the row's total, without LDS traffic.
+__device__ inline float row16_sum(float a) {
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true));
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true));
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, true));
+  a += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x140, 0xF, 0xF, true));
+  return a;
+}
 
 constexpr int kThreads = 256;
 constexpr int kPairs = kThreads / 16;     // (row, head) pairs per workgroup
@@ -57,30 +68,52 @@ __global__ __launch_bounds__(kThreads) void camera_attn_kernel(CamParams p) {
     qf[2 * e] = lo_f(qv[e]);
     qf[2 * e + 1] = hi_f(qv[e]);
   }
+  // keys in blocks of four: the block's k and v loads go out together (one
+  // memory latency per block instead of two per key); indices past t_cam are
+  // clamped for the loads and their weights forced to zero
   float m = -INFINITY, l = 0.0f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < p.t_cam; ++j) {
-    const int64_t off = (cam0 + j) * p.kv_st + (int64_t)head * p.kv_sh + 8 * li;
-    const u32x4 kv = *(const u32x4*)(p.k + off);
-    const u32x4 vv = *(const u32x4*)(p.v + off);
-    float d = 0.0f;
+  for (int j0 = 0; j0 < p.t_cam; j0 += 4) {
+    u32x4 kv[4], vv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      d = fmaf(qf[2 * e], lo_f(kv[e]), d);
-      d = fmaf(qf[2 * e + 1], hi_f(kv[e]), d);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t off = (cam0 + min(j0 + u, p.t_cam - 1)) * p.kv_st + (int64_t)head * p.kv_sh + 8 * li;
+      kv[u] = *(const u32x4*)(p.k + off);
+      vv[u] = *(const u32x4*)(p.v + off);
+    }
+    float sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(qf[2 * e], lo_f(kv[u][e]), d);
+        d = fmaf(qf[2 * e + 1], hi_f(kv[u][e]), d);
+      }
+      sv[u] = d;
     }
 #pragma unroll
-    for (int s = 8; s >= 1; s >>= 1) d += __shfl_xor(d, s, 16);
-    const float sv = d * p.scale_log2;
-    const float mn = fmaxf(m, sv);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);       // 0 on the first key (m = -inf)
-    const float pr = __builtin_amdgcn_exp2f(sv - mn);
-    l = fmaf(l, alpha, pr);
+    for (int u = 0; u < 4; ++u) sv[u] = row16_sum(sv[u]);
+    float mx = m;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = fmaf(acc[2 * e], alpha, pr * lo_f(vv[e]));
-      acc[2 * e + 1] = fmaf(acc[2 * e + 1], alpha, pr * hi_f(vv[e]));
+    for (int u = 0; u < 4; ++u) {
+      sv[u] = (j0 + u < p.t_cam) ? sv[u] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[u]);
     }
-    m = mn;
+    const float alpha = __builtin_amdgcn_exp2f(m - mx);        // 0 on the first block (m = -inf)
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float pr = __builtin_amdgcn_exp2f(sv[u] - mx);       // 0 for the padded keys
+      l += pr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(pr, lo_f(vv[u][e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(pr, hi_f(vv[u][e]), acc[2 * e + 1]);
+      }
+    }
+    m = mx;
   }
   const float inv = 1.0f / l;
   u32x4 o;
