@@ -353,3 +353,50 @@ def test_camera_rejects(kw, code):
 def test_camera_noop():
     assert _cam(n_tok=0, q=None, k=None, v=None, o=None) == 0
     assert lib.camera_cross_attn(None, None) == 1
+
+
+# ---------------------------------------------- binding matches the header ----
+
+_C_TYPES = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "float": ctypes.c_float,
+            "double": ctypes.c_double}
+
+
+def _header_structs():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"typedef struct (\w+) \{(.*?)\} \w+;", src, flags=re.S):
+        fields = []
+        for decl in m.group(2).split(";"):
+            decl = decl.strip()
+            if not decl:
+                continue
+            typ, names = re.match(r"(.*?)(\**\s*\w+(?:\s*,\s*\**\s*\w+)*)$", decl).groups()
+            for nm in names.split(","):
+                ptr = "*" in typ or "*" in nm
+                fields.append((nm.replace("*", "").strip(), "ptr" if ptr else typ.replace("const", "").strip()))
+        out[m.group(1)] = fields
+    return out
+
+
+@pytest.mark.parametrize("cname,py", [
+    ("segc_cache", "SegcCache"), ("segc_attn_args", "SegcAttnArgs"),
+    ("segc_attn_bwd_args", "SegcAttnBwdArgs"), ("segc_camera_args", "SegcCameraArgs"),
+])
+def test_binding_structs_match_header(cname, py):
+    want = _header_structs()[cname]
+    got = getattr(sc, py)._fields_
+    assert [n for n, _ in got] == [n for n, _ in want], cname
+    for (n, t), (_, ct) in zip(got, want):
+        if ct == "ptr":
+            assert ctypes.sizeof(t) == ctypes.sizeof(ctypes.c_void_p), n
+        else:
+            assert t is _C_TYPES[ct], (n, ct, t)
+
+
+def test_binding_argtypes_match_header_arity():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for m in re.finditer(r"^(?:int|const char\*)\s+(\w+)\s*\((.*?)\);", src, flags=re.M | re.S):
+        name, params = m.group(1), m.group(2).strip()
+        n_params = 0 if params in ("", "void") else params.count(",") + 1
+        argtypes = getattr(lib, name).argtypes
+        assert len(argtypes or []) == n_params, (name, n_params, argtypes)
