@@ -399,11 +399,17 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info
         }
       }
   }
-  float mx = s[0][0];
+  // tile max as a tree of 3-input maxima (depth 4 rather than a 16-deep chain)
+  float m1[11];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+  for (int i = 0; i < 10; ++i) {
+    const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
+    m1[i] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[e >> 4][e & 15]);
+  }
+  m1[10] = fmaxf(s[1][14], s[1][15]);
+  const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]), m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+  const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]), m2d = fmaxf(m1[9], m1[10]);
+  float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
   mx = xhalf_max(mx);
   const float mnew = fmaxf(rs.m, mx);
   const bool need = (mnew - rs.m) * c > kTau;          // false for -inf/-inf (NaN)
@@ -461,6 +467,9 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb, o[db], 0, 0, 0);
     }
   }
+  // use the sum here: otherwise its adds sink below the staging branch that
+  // follows and run, with no products left to hide them, before the barrier
+  asm volatile("" :: "v"(ls));
   rs.l += ls;
 }
 
