@@ -42,8 +42,11 @@
 //    blocks) with their operand reads scheduled 4 MFMAs ahead;
 //  * each staging wave loads a 16-row group of a tile: with frames of a
 //    multiple of 16 tokens a group never straddles a frame, so its base
-//    address is wave-uniform and lanes only add 32-bit offsets; rows past the
-//    end are clamped to the last valid row (finite data) and masked;
+//    address is wave-uniform (SGPRs) and a whole group is loaded in the
+//    scalar-base form with loop-invariant 32-bit lane offsets: the staging
+//    waves wait at every barrier for each other, so their per-tile address
+//    work is on the critical path; rows past the end are clamped to the last
+//    valid row (finite data) and masked;
 //  * INT8 history rows (codes and scales) are direct-loaded into one of two
 //    staging areas and dequantised to bf16(code * scale) into the tile by the
 //    wave that loaded them, so the MFMA path is the same for both cache types;
@@ -232,8 +235,11 @@ __device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ (5 * (r & 3))
 // (stage_finish) before the barrier that publishes the tile. M0 holds the
 // LDS base; gfx9 needs one wait state between an SALU write of M0 and an
 // LDS-DMA load. Nothing else in this kernel keeps a value in M0.
+// A generic pointer into LDS holds the LDS byte address in its low 32 bits
+// (the shared aperture is 4 GB aligned; the address-space cast would add a
+// null check per use, which these never-null tile pointers do not need).
 __device__ inline uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)p);
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 __device__ inline void dload16(const void* g, const char* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -242,6 +248,12 @@ __device__ inline void dload16(const void* g, const char* lds_base) {
 __device__ inline void dload4(const void* g, const char* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the load's scalar-base form: no per-lane 64-bit address math).
+__device__ inline void dload16_s(uint32_t voff, uint64_t sbase, const char* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory", "m0");
 }
 // A kernel-argument pointer as a wave-uniform value (keeps a per-lane choice
 // between two such pointers a register select, not a per-lane load).
@@ -260,6 +272,33 @@ __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, in
                                   char* buf, char* raw) {
   const Group g = group_at(p, tl, w, head);
   if (!tl.hist || !p.hist_int8) {
+    if (g.lim >= RW - 1 && !g.generic) {
+      // a whole group (no clamping) of consecutive rows of one frame or of the
+      // current rows: a uniform base per tensor, and per-lane offsets that only
+      // depend on the lane and the row pitch (4 rows per instruction; group row
+      // r = 4 e + lane / 16 is also the tile row modulo 16, which sets the swizzle)
+      uint64_t kb, vb;
+      uint32_t ks, vs;
+      if (tl.hist) {
+        kb = uniform_ptr((const char*)p.hk + g.row0 * 256);
+        vb = uniform_ptr((const char*)p.hv + g.row0 * 256);
+        ks = vs = 256;
+      } else {
+        kb = uniform_ptr(p.k + g.row0 * p.k_st + head * p.k_sh);
+        vb = uniform_ptr(p.v + g.row0 * p.v_st + head * p.v_sh);
+        ks = (uint32_t)p.k_st * 2;
+        vs = (uint32_t)p.v_st * 2;
+      }
+      const uint32_t lrow = lane >> 4, pc = lane & 15;
+#pragma unroll
+      for (int e = 0; e < RW / 4; ++e) {
+        const uint32_t r = 4 * e + lrow;
+        char* dst = buf + (RW * w + 4 * e) * 256;
+        dload16_s(r * ks + ((pc ^ r) << 4), kb, dst + KOFF);
+        dload16_s(r * vs + ((pc ^ (5 * (lrow & 3))) << 4), vb, dst + VOFF);
+      }
+      return 2 * (RW / 4);
+    }
     // all addresses first: a per-lane slot lookup (generic path) is an
     // ordinary load, and waiting for it would also drain earlier direct loads
     const char *krow[RW / 4], *vrow[RW / 4];
