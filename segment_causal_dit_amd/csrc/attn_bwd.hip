@@ -80,10 +80,28 @@ __device__ inline int t_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4)
 // lds_base + 16 l), issued from inline assembly so that the compiler does not
 // drain it before unrelated LDS reads; M0 holds the LDS base (one wait state
 // after the SALU write). Nothing else in these kernels keeps a value in M0.
+// A generic pointer into LDS holds the LDS byte address in its low 32 bits
+// (the shared aperture is 4 GB aligned; the address-space cast would add a
+// null check per use, which these never-null tile pointers do not need).
+__device__ inline uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
 __device__ inline void dload16(const void* g, const char* lds_base) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(a)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds_addr(lds_base))
                : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the load's scalar-base form: no per-lane 64-bit address math).
+__device__ inline void dload16_s(uint32_t voff, uint64_t sbase, const char* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory", "m0");
+}
+// A wave-uniform address as SGPRs.
+__device__ inline uint64_t uniform_addr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 __device__ inline void dload_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -367,6 +385,20 @@ __global__ __launch_bounds__(QT, 2) void dq_kernel(AttnBwdParams p) {
 template <int RPW>
 __device__ inline void stage_pair(const uint16_t* a, int64_t a_st, const uint16_t* b, int64_t b_st,
                                   int row0, int nvalid, int w, int lane, char* dstA, char* dstB) {
+  if (RPW * w + RPW <= nvalid) {
+    // a whole group (no clamping): uniform bases and loop-invariant lane offsets
+    const uint64_t ab = uniform_addr(a + (int64_t)(row0 + RPW * w) * a_st);
+    const uint64_t bb = uniform_addr(b + (int64_t)(row0 + RPW * w) * b_st);
+    const uint32_t lrow = lane >> 4, pc = lane & 15;
+#pragma unroll
+    for (int e = 0; e < RPW / 4; ++e) {
+      const uint32_t r = 4 * e + lrow;
+      const uint32_t sw = (pc ^ swz(RPW * w + r)) << 4;
+      dload16_s(r * (uint32_t)a_st * 2 + sw, ab, dstA + (RPW * w + 4 * e) * 256);
+      dload16_s(r * (uint32_t)b_st * 2 + sw, bb, dstB + (RPW * w + 4 * e) * 256);
+    }
+    return;
+  }
   const char* ar[RPW / 4];
   const char* br[RPW / 4];
 #pragma unroll
