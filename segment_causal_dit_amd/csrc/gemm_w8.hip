@@ -67,10 +67,27 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 // lds_base + 16 l), from inline assembly so that the compiler does not drain
 // it before unrelated LDS reads; M0 holds the LDS base. Completion is awaited
 // explicitly with vmcnt.
+// (A generic pointer into LDS holds the LDS byte address in its low 32 bits:
+// the shared aperture is 4 GB aligned, and the address-space cast would add a
+// null check per use.)
+__device__ inline uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
 __device__ inline void dload16(const void* g, const char* lds_base) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(a)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds_addr(lds_base))
                : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the load's scalar-base form: no per-lane 64-bit address math).
+__device__ inline void dload16_s(uint32_t voff, uint64_t sbase, const char* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory", "m0");
+}
+__device__ inline uint64_t uniform_addr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
 // Four signed codes (one dword) -> four bf16, exact.
@@ -130,23 +147,48 @@ __global__ __launch_bounds__(NTH, 2) void w8a16_kernel(W8GemmParams p) {
   const char* xsrc[32 / RPL];
   const char* wsrc[32 / RPL];
   int m0, n0;
+  bool full;                            // every activation row of the tile exists
   // staging: wave w loads tile rows 32 w .. + 31 of both operands, RPL rows
-  // per direct load (lane l: row l / CH, physical chunk l % CH)
+  // per direct load (lane l: row l / CH, physical chunk l % CH). Full tiles
+  // use uniform row-group bases and per-lane 32-bit offsets, which depend on
+  // the lane and e only; the last, ragged row tile clamps rows per lane.
+  uint32_t xoff[32 / RPL], woff[32 / RPL];
+#pragma unroll
+  for (int e = 0; e < 32 / RPL; ++e) {
+    const int row = 32 * w + RPL * e + lane / CH;
+    const uint32_t sw = ((lane % CH) ^ g_swz(row)) << 4;
+    xoff[e] = (uint32_t)(lane / CH) * (uint32_t)p.ldx * 2 + sw;
+    woff[e] = (uint32_t)(lane / CH) * (uint32_t)p.K * 2 + sw;
+  }
   auto set_tile = [&](int logical) {
     tile_of(p, logical, m0, n0);
+    full = m0 + TM <= p.M;
+    if (!full) {
 #pragma unroll
-    for (int e = 0; e < 32 / RPL; ++e) {
-      const int row = 32 * w + RPL * e + lane / CH;
-      const int sw = ((lane % CH) ^ g_swz(row)) << 4;
-      xsrc[e] = (const char*)(p.x + (int64_t)min(m0 + row, p.M - 1) * p.ldx) + sw;
-      wsrc[e] = (const char*)(p.wbf + (int64_t)(n0 + row) * p.K) + sw;
+      for (int e = 0; e < 32 / RPL; ++e) {
+        const int row = 32 * w + RPL * e + lane / CH;
+        const int sw = ((lane % CH) ^ g_swz(row)) << 4;
+        xsrc[e] = (const char*)(p.x + (int64_t)min(m0 + row, p.M - 1) * p.ldx) + sw;
+        wsrc[e] = (const char*)(p.wbf + (int64_t)(n0 + row) * p.K) + sw;
+      }
     }
   };
   auto issue = [&](int kt, char* stage) {
+    if (full) {
 #pragma unroll
-    for (int e = 0; e < 32 / RPL; ++e) {
-      dload16(xsrc[e] + kt * ROWB, stage + (32 * w + RPL * e) * ROWB);
-      dload16(wsrc[e] + kt * ROWB, stage + XT_BYTES + (32 * w + RPL * e) * ROWB);
+      for (int e = 0; e < 32 / RPL; ++e) {
+        const int r0 = 32 * w + RPL * e;                 // first tile row of the load
+        const uint64_t xb = uniform_addr(p.x + (int64_t)(m0 + r0) * p.ldx + kt * TK);
+        const uint64_t wb = uniform_addr(p.wbf + (int64_t)(n0 + r0) * p.K + kt * TK);
+        dload16_s(xoff[e], xb, stage + r0 * ROWB);
+        dload16_s(woff[e], wb, stage + XT_BYTES + r0 * ROWB);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32 / RPL; ++e) {
+        dload16(xsrc[e] + kt * ROWB, stage + (32 * w + RPL * e) * ROWB);
+        dload16(wsrc[e] + kt * ROWB, stage + XT_BYTES + (32 * w + RPL * e) * ROWB);
+      }
     }
   };
   auto wait_newer = [&](int newer) {
