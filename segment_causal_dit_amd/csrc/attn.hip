@@ -614,6 +614,12 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     char* const nx1 = smem + (bc == NBUF - 1 ? 0 : bc + 1) * BUF_BYTES;
     char* const nx2 = smem + (bc == 0 ? NBUF - 1 : bc - 1) * BUF_BYTES;
     const int* info = (const int*)(cur + IOFF);
+    // nothing is outstanding here (the barrier drained LDS; scalar loads are
+    // consumed where issued), but a scalar load hoisted before the loop would
+    // otherwise make the compiler wait for every LDS read ahead of the first
+    // product of each tile (scalar and LDS loads share a counter, and scalar
+    // loads complete out of order)
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
     int issued = 0;
     if (stager && t + 2 < n_tiles)
       issued = stage_issue(p, tile_at(p, t + 2, cur_end), w, lane, head, nx2, (t & 1) ? raw1 : raw0);
