@@ -75,7 +75,7 @@ def _gpu_backward(inp, do_bits, sm_scale=None):
 
 
 @pytest.mark.parametrize("name", ["bwd_small", "bwd_one", "bwd_text", "c0_packed3", "mid_nocache",
-                                  "bwd_mid"])
+                                  "bwd_mid", "bwd_seg16"])
 def test_gradients_match_oracle(name):
     _say("bwd", name)
     inp = workloads.make_inputs(name)

@@ -26,7 +26,7 @@ sc = pytest.importorskip("segment_causal_dit_amd._lib")
 
 MAX_ERR, MEAN_ERR, LSE_ERR = 1e-2, 1e-3, 5e-3
 SMALL = ["c0", "c0_int8", "c0_win3", "c0_pad", "c0_packed3",
-         "mid_int8", "mid_bf16", "mid_packed", "mid_nocache"]
+         "mid_int8", "mid_bf16", "mid_packed", "mid_nocache", "max_seg16"]
 
 
 def _say(*a):

@@ -106,6 +106,19 @@ class Config:
 _INV_SQRT_D = 1.0 / math.sqrt(HEAD_DIM)
 _FULL = (22, 40)
 
+# (text_len, text_valid, n_frames) of 16 packed segments, for the cases at
+# the segment limit of one call
+_SEG16 = ((8, 8, 1), (0, 0, 2), (5, 3, 1), (12, 12, 0), (7, 7, 1), (3, 1, 2), (0, 0, 1), (16, 9, 1),
+          (9, 9, 1), (1, 1, 1), (4, 4, 0), (6, 2, 2), (0, 0, 1), (11, 11, 1), (2, 2, 1), (10, 6, 1))
+
+
+def _seg_list(t0):
+    out, t = [], t0
+    for tl, tv, nf in _SEG16:
+        out.append(SegSpec(tl, tv, nf, t))
+        t += nf
+    return tuple(out)
+
 CONFIGS = {
     # 2 heads, 16 text tokens, 4x6 grid; two cached segments of 2 frames each
     # (t = 0..3) and a current segment of 2 frames (t = 4, 5); BF16 cache.
@@ -149,6 +162,10 @@ VARIANTS = {
                          hist_t=(0, 1, 2), cache_dtype="bf16", q_scale=_INV_SQRT_D),
     "mid_nocache": Config("mid_nocache", 2, (7, 13), (SegSpec(45, 45, 4, 0),),
                           q_scale=_INV_SQRT_D),
+    # the most segments one call takes (16), over an INT8 history that the
+    # run appends to: text-only segments, segments without text, padded text
+    "max_seg16": Config("max_seg16", 2, (4, 8), _seg_list(2), hist_t=(0, 1), cache_dtype="int8",
+                        extra_slots=17, q_scale=_INV_SQRT_D, append=True),
 }
 
 # Packed training form (segment forcing): every segment present, no cache.
@@ -174,6 +191,7 @@ TRAIN = {
     "bwd_one": Config("bwd_one", 3, (10, 13), (SegSpec(0, 0, 5, 0),), sm_scale=_INV_SQRT_D),
     "bwd_text": Config("bwd_text", 2, (6, 7), (SegSpec(64, 64, 4, 0), SegSpec(64, 33, 0, 4),
                                                SegSpec(1, 1, 3, 4)), q_scale=_INV_SQRT_D),
+    "bwd_seg16": Config("bwd_seg16", 2, (4, 8), _seg_list(0), q_scale=_INV_SQRT_D),
 }
 
 ALL = dict(CONFIGS, **VARIANTS, **TRAIN)
