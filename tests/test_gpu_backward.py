@@ -16,7 +16,11 @@ that see many, so the errors are measured against the rms of each
 (row, head) of the fp64 gradient: max <= 2^-4 (the largest over 10^5..10^9
 elements of a 1.6e-3-wide error, whose tail grows with |g| / rms_row, stays
 below about 2.5e-2) and mean <= 2^-8 (2.4x the expected 1.6e-3). Keys no
-query sees have dk = dv = 0 exactly, and are left out of the ratios.
+query sees have dk = dv = 0 exactly, and are left out of the ratios. The
+random packed forms also hold rows that see only a few keys, whose dq (and
+the dk of their keys) can be much smaller than the terms that cancel in it:
+there each element may instead stay within the error that delta, formed from
+the forward's bf16 output, carries into it (_delta_bounds).
 """
 
 import sys
@@ -54,15 +58,51 @@ def _invisible_keys(cfg):
     return np.asarray(rows, dtype=np.int64)
 
 
-def _check(name, got, want):
-    """Errors relative to the rms of each (row, head) of the fp64 gradient."""
+def _check(name, got, want, bound=None):
+    """Errors relative to the rms of each (row, head) of the fp64 gradient.
+    With `bound` (per element, from _delta_bounds), an element whose derived
+    rounding bound exceeds the rms bar is held to that bound instead."""
     rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
     live = np.broadcast_to(rms > 0, want.shape)
-    rel = np.abs(got - want)[live] / np.broadcast_to(rms, want.shape)[live]
+    err = np.abs(got - want)
+    rel = err[live] / np.broadcast_to(rms, want.shape)[live]
     mx, mean = float(rel.max()), float(rel.mean())
     _say("  %s: max %.4f, mean %.5f of the row rms" % (name, mx, mean))
-    assert mx <= MAX_REL, name
     assert mean <= MEAN_REL, name
+    if bound is None:
+        assert mx <= MAX_REL, name
+    else:
+        allowed = np.maximum(MAX_REL * np.broadcast_to(rms, want.shape), bound)
+        worst = float((err[live] / allowed[live]).max())
+        _say("  %s: max %.3f of max(rms bar, derived bound)" % (name, worst))
+        assert worst <= 1.0, name
+
+
+def _delta_bounds(q, k, v, do, segs, sm_scale):
+    """Per-element bounds on the dq and dk errors that come from delta.
+    The kernel forms delta_i = do_i . o_i from the forward's bf16 output
+    (relative error <= 2^-8 per element of o, the forward's error included),
+    so |delta' - delta| <= eps_i = 2^-8 sum_d |do_id o_id|; with p_ij rounded
+    to bf16 inside ds_ij = p_ij (dp_ij - delta_i) that gives
+    |ds' - ds| <= p_ij (eps_i + 2^-8 |dp_ij - delta_i|), and
+    dq_i = sm_scale sum_j ds_ij k_j, dk_j = sm_scale sum_i ds_ij q_i carry it
+    with |k| and |q|. Rows that see few keys can have a dq far smaller than
+    these terms (ds nearly cancels across the keys), where an rms-relative bar
+    cannot hold."""
+    n, nh, _ = q.shape
+    vis = oracle.visible_mask(0, segs, n)
+    o, lse = oracle.joint_attn(q, k, v, segs, sm_scale=sm_scale)
+    bq, bk = np.zeros_like(q), np.zeros_like(k)
+    for h in range(nh):
+        s = sm_scale * q[:, h] @ k[:, h].T
+        p = np.where(vis, np.exp(np.where(vis, s, 0.0) - lse[h][:, None]), 0.0)
+        eps = 2.0 ** -8 * np.abs(do[:, h] * o[:, h]).sum(-1)
+        dp = do[:, h] @ v[:, h].T
+        delta = (do[:, h] * o[:, h]).sum(-1)
+        t = p * (eps[:, None] + 2.0 ** -8 * np.abs(dp - delta[:, None]))
+        bq[:, h] = sm_scale * t @ np.abs(k[:, h])
+        bk[:, h] = sm_scale * t.T @ np.abs(q[:, h])
+    return bq, bk
 
 
 def _gpu_backward(inp, do_bits, sm_scale=None):
@@ -88,6 +128,27 @@ def test_gradients_match_oracle(name):
     for nm, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
         _check(nm, to_f64(g), w)
     dead = _invisible_keys(inp.cfg)
+    if len(dead):
+        assert not bits(dk)[dead].any() and not bits(dv)[dead].any()
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_gradients_random_packed_configs(i):
+    # seeded random packed forms (no cache): 1-16 segments, text padding,
+    # text-only and text-free segments, frame sizes on and off 16 tokens
+    cfg = workloads.random_config(i, history=False)
+    _say("bwd", cfg)
+    inp = workloads.make_inputs(cfg)
+    do_bits = workloads.upstream_grad(cfg)
+    _, dq, dk, dv = _gpu_backward(inp, do_bits)
+    q, k, v = oracle_inputs(inp)
+    segs = [oracle.Segment(*s) for s in inp.segments]
+    do = oracle.bf16_bits_to_f64(do_bits)
+    want = oracle.joint_attn_backward(q, k, v, segs, do, sm_scale=cfg.sm_scale)
+    bq, bk = _delta_bounds(q, k, v, do, segs, cfg.sm_scale)
+    for nm, g, w, b in zip(("dq", "dk", "dv"), (dq, dk, dv), want, (bq, bk, None)):
+        _check(nm, to_f64(g), w, b)
+    dead = _invisible_keys(cfg)
     if len(dead):
         assert not bits(dk)[dead].any() and not bits(dv)[dead].any()
 

@@ -157,9 +157,12 @@ def _check_chain(name):
         nf = len(cfg.hist_t)
         g, h = cfg.tokens_per_frame, cfg.n_heads
         kf = k[start + tl:start + tl + n].reshape(s.n_frames, g, h, HEAD_DIM).transpose(0, 2, 1, 3)
-        kc, ks = oracle.quantise_int8(kf)
-        assert np.array_equal(r.cache.k[nf:nf + s.n_frames].cpu().numpy(), kc)
-        assert np.array_equal(r.cache.k_scale[nf:nf + s.n_frames].cpu().numpy(), ks)
+        if cfg.cache_dtype == "int8":
+            kc, ks = oracle.quantise_int8(kf)
+            assert np.array_equal(r.cache.k[nf:nf + s.n_frames].cpu().numpy(), kc)
+            assert np.array_equal(r.cache.k_scale[nf:nf + s.n_frames].cpu().numpy(), ks)
+        else:
+            assert np.array_equal(bits(r.cache.k[nf:nf + s.n_frames]), oracle.f64_to_bf16_bits(kf))
         assert list(r.cache.slot_t[nf:nf + s.n_frames]) == list(range(s.t0, s.t0 + s.n_frames))
 
 
@@ -171,6 +174,14 @@ def test_chain_small(name):
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
 def test_chain_full_size(name):
     _check_chain(name)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_chain_random_small_configs(i):
+    # seeded random structure: 1-16 segments of random text / padding / frame
+    # counts, frame sizes on and off the 16-token grouping, BF16 or INT8
+    # history with a random window and an optional append
+    _check_chain(workloads.random_config(i))
 
 
 def test_attention_identical_int8_inputs_mid():

@@ -196,6 +196,38 @@ TRAIN = {
 
 ALL = dict(CONFIGS, **VARIANTS, **TRAIN)
 
+_RANDOM_GRIDS = ((2, 8), (4, 4), (3, 5), (4, 6), (5, 7), (8, 8))   # 16, 16, 15, 24, 35, 64 tokens
+
+
+def random_config(i, history=True):
+    """A small seeded configuration for parity sweeps (PCG64(42 + 100 + i)).
+    Every segment holds at least one frame or two valid text rows, so every
+    query row sees at least two keys (a query with one visible key has
+    gradients that vanish only by cancellation); history frames precede the
+    segments in time."""
+    rng = np.random.Generator(np.random.PCG64(SEED + 100 + i))
+    grid = _RANDOM_GRIDS[int(rng.integers(len(_RANDOM_GRIDS)))]
+    g = grid[0] * grid[1]
+    n_hist = int(rng.integers(0, 5)) if history else 0
+    segs, t = [], n_hist
+    for _ in range(int(rng.integers(1, 17))):
+        nf = int(rng.integers(0, 3))
+        tl = int(rng.integers(0, 41))
+        tv = int(rng.integers(0, tl + 1)) if tl else 0
+        if nf == 0 and tv < 2:
+            tl, tv = max(tl, 2), 2
+        segs.append(SegSpec(tl, tv, nf, t))
+        t += nf
+    cache = "none" if n_hist == 0 else ("int8" if rng.integers(2) else "bf16")
+    append = cache != "none" and segs[0].n_frames > 0 and bool(rng.integers(2))
+    budget = -1 if n_hist == 0 or rng.integers(2) else int(rng.integers(1, n_hist + 1))
+    unscaled = bool(rng.integers(2))
+    return Config("random%d" % i, int(rng.integers(1, 4)), grid, tuple(segs),
+                  hist_t=tuple(range(n_hist)), cache_dtype=cache,
+                  extra_slots=segs[0].n_frames if append else 0, budget=budget,
+                  q_scale=1.0 if unscaled else _INV_SQRT_D,
+                  sm_scale=_INV_SQRT_D if unscaled else 1.0, append=append)
+
 
 # ---------------------------------------------------------------- draws ----
 
