@@ -100,3 +100,21 @@ def test_general_path_full_size_sampled_chunks_and_strides():
         cam = slice(c * t_cam, (c + 1) * t_cam)
         want = oracle.camera_cross_attn(f(q[rows]), f(k[cam]), f(v[cam]), tpc, t_cam, 1.0 / np.sqrt(HEAD_DIM))
         _check(_f64(o[rows]), want, f(v[cam]))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_shapes(i):
+    # seeded random rows, heads, chunk sizes (ragged last chunk) and camera
+    # tokens per chunk; one token per chunk must give v bit for bit
+    rng = np.random.default_rng(3000 + i)
+    n, h = int(rng.integers(1, 3000)), int(rng.integers(1, 5))
+    tpc, t_cam = int(rng.integers(1, 1000)), int(rng.integers(1, 9))
+    _say("camera random", n, h, tpc, t_cam)
+    q, k, v = _inputs(n, h, tpc, t_cam, 40 + i)
+    o = sc.camera_cross_attn(_bf(q), _bf(k), _bf(v), tpc, 1.0 / np.sqrt(HEAD_DIM))
+    torch.cuda.synchronize()
+    if t_cam == 1:
+        assert np.array_equal(_bits(o), np.repeat(v, tpc, axis=0)[:n])
+    else:
+        f = oracle.bf16_bits_to_f64
+        _check(_f64(o), oracle.camera_cross_attn(f(q), f(k), f(v), tpc, t_cam, 1.0 / np.sqrt(HEAD_DIM)), f(v))

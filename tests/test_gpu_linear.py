@@ -96,3 +96,19 @@ def test_full_size_sampled_rows(name):
     rows = np.unique(np.concatenate([[0, 255, 256, m - 1], rng.integers(0, m, 92)]))
     _check(_f64(y[torch.from_numpy(rows).cuda()]), x, codes, scale, bias, rows=rows)
     assert bool(torch.isfinite(y).all())
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_shapes(i):
+    # seeded random shapes inside the kernel's tiling rules (n a multiple of
+    # 256, k of 64): ragged row tiles, several k steps, with and without bias
+    rng = np.random.default_rng(1000 + i)
+    m, n, k = int(rng.integers(1, 700)), 256 * int(rng.integers(1, 5)), 64 * int(rng.integers(1, 17))
+    with_bias = bool(rng.integers(2))
+    _say("linear random", m, n, k, with_bias)
+    x, codes, scale, bias = workloads.linear_inputs(m, n, k, seed=2000 + i)
+    bias = bias if with_bias else None
+    y = sc.w8a16_linear(_bf(x), torch.from_numpy(codes).cuda(), torch.from_numpy(scale).cuda(),
+                        torch.from_numpy(bias).cuda() if bias is not None else None)
+    torch.cuda.synchronize()
+    _check(_f64(y), x, codes, scale, bias)
