@@ -77,6 +77,24 @@ def test_rope_other_split_and_theta():
     assert np.array_equal(bits(x), want)
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_rope_random_shapes(i):
+    # seeded rows, heads, positions, theta and axis split: bit-exact
+    rng = np.random.default_rng(4000 + i)
+    n, h = int(rng.integers(1, 5000)), int(rng.integers(1, 9))
+    dims = [(16, 56, 56), (32, 48, 48), (64, 32, 32)][int(rng.integers(3))]
+    theta = [256.0, 10000.0][int(rng.integers(2))]
+    pos = np.stack([rng.integers(0, 2000, n), rng.integers(0, 100, n), rng.integers(0, 100, n)],
+                   axis=1).astype(np.int32)
+    _say("rope random", n, h, dims, theta)
+    xb = workloads.normal_bf16(50 + i, (n, h, HEAD_DIM))
+    x = _bf(xb)
+    sc.rope3d_apply(x, torch.from_numpy(pos).cuda(), theta=theta, dims=dims)
+    want = oracle.f64_to_bf16_bits(oracle.rope3d_bf16(xb, pos, theta=theta, dims=dims))
+    got = bits(x)
+    assert np.array_equal(got, want), "%d of %d differ" % ((got != want).sum(), got.size)
+
+
 # ---------------------------------------------------------------- append ----
 
 def _adversarial_rows(n_rows, seed):
@@ -121,6 +139,38 @@ def test_append_bit_exact_with_ring_wrap(dtype):
             assert np.array_equal(bits(cache.v[slot]), vf)
     for slot in (1, 2):
         assert not cache.k[slot].view(torch.uint8).cpu().numpy().any()
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_append_random_shapes(i):
+    # seeded frame sizes, heads, frame counts and ring positions, both cache
+    # types, adversarial rows (quotients next to half-integers) half the time
+    rng = np.random.default_rng(5000 + i)
+    g, h, nf = int(rng.integers(1, 201)), int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    n_slots = nf + int(rng.integers(0, 4))
+    first = int(rng.integers(0, n_slots))
+    dtype = ["int8", "bf16"][int(rng.integers(2))]
+    _say("append random", g, h, nf, n_slots, first, dtype)
+    if rng.integers(2):
+        rows = _adversarial_rows(nf * g * h, 60 + i).reshape(nf * g, h, HEAD_DIM)
+    else:
+        rows = workloads.normal_bf16(60 + i, (nf * g, h, HEAD_DIM), 3.0)
+    vrows = workloads.normal_bf16(70 + i, (nf * g, h, HEAD_DIM))
+    cache = sc.KVCache(n_slots, h, g, dtype, "cuda")
+    sc.kv_cache_append(cache, first, _bf(rows), _bf(vrows))
+    torch.cuda.synchronize()
+    for f in range(nf):
+        slot = (first + f) % n_slots
+        kf = rows[f * g:(f + 1) * g].transpose(1, 0, 2)
+        vf = vrows[f * g:(f + 1) * g].transpose(1, 0, 2)
+        if dtype == "int8":
+            for got_c, got_s, src in ((cache.k, cache.k_scale, kf), (cache.v, cache.v_scale, vf)):
+                c, sc_ = oracle.quantise_int8(oracle.bf16_bits_to_f64(src))
+                assert np.array_equal(got_c[slot].cpu().numpy(), c)
+                assert np.array_equal(got_s[slot].cpu().numpy(), sc_)
+        else:
+            assert np.array_equal(bits(cache.k[slot]), kf)
+            assert np.array_equal(bits(cache.v[slot]), vf)
 
 
 # ------------------------------------------------------------- attention ----
