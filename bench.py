@@ -669,7 +669,7 @@ def main():
         counters_workload(args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the attention would shard by heads; see the design notes).", file=sys.stderr)
         sys.exit(2)
 

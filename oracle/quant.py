@@ -4,7 +4,7 @@ Source: "Hy-Nomas: Towards Free-Form Interactive World Generation", section
 "Single-GPU Low-Memory Inference" (cached keys and values are stored in INT8
 while attention is computed in BF16); "Tencent Opens Hy-Nomas ...", section
 "How the RTX 4090 configuration saves memory" (INT8 KV cache, BF16 attention).
-The pages do not give the quantiser; this build's scheme is:
+The pages do not give the quantiser; the scheme taken here is:
 
 * one fp32 scale per (token, head) over its 128 values:
   scale = fp32(absmax / 127), IEEE fp32 division;
@@ -12,7 +12,7 @@ The pages do not give the quantiser; this build's scheme is:
 * a token-head whose values are all zero gets scale 0 and all-zero codes;
 * dequantised value = code * scale; where attention runs in BF16 the value
   fed to it is bf16(fp32(code * scale)): the exact product rounded to fp32,
-  then to bf16, both round-to-nearest-even (this build's reading).
+  then to bf16, both round-to-nearest-even (the reading taken here).
 
 Emulating fp32 division: both operands are fp32 values, so the float64
 quotient rounded to fp32 equals the IEEE fp32 quotient (float64 carries
