@@ -54,8 +54,8 @@ extern "C" {
 #define SEGC_MAX_SEG  16     /* packed segments per attention call */
 
 /*
- * A per-layer KV cache of latent frames ("the layer's KV cache supplying
- * context from earlier segments", model card, section "Segment-Autoregressive
+ * A per-layer KV cache of latent frames (the keys and values of earlier
+ * segments that each layer reuses; model card, section "Segment-Autoregressive
  * Diffusion Transformer"). Holds video tokens only, K after RoPE, V as is.
  *
  * Memory (all caller-owned device memory):
@@ -111,7 +111,7 @@ int rope3d_apply(const void* x_in, void* x_out, int64_t n_tok, int32_t n_heads,
  * kv_cache_append -- write the current segment's video K (after RoPE) and V
  * into cache slots, quantising to INT8 when the cache is SEGC_INT8.
  * Source: model card, section "Segment-Autoregressive Diffusion Transformer"
- * (cached keys and values are reused when generation advances) and section
+ * (cached keys and values serve again as generation moves on) and section
  * "Single-GPU Low-Memory Inference" (cached keys/values stored in INT8, BF16
  * compute). The INT8 scheme is this library's: per (token, head)
  *   scale = fp32(max|x| / 127)             (IEEE fp32 division)
@@ -219,11 +219,11 @@ int w8a16_linear(const void* x, int64_t ldx, const int8_t* w, int64_t ldw, const
 /*
  * camera_cross_attn -- per-latent-frame camera cross-attention of the video
  * rows.
- * Source: model card, section "Text and Camera Conditioning" (camera
- * extrinsics grouped over four video frames into one 64-dimensional input
- * per latent frame; at every double-stream block the video tokens query the
- * projected camera features through cross-attention after the video MLP;
- * per-chunk camera attention with a chunk size of one latent frame).
+ * Source: model card, section "Text and Camera Conditioning" (four video
+ * frames' camera extrinsics form one 64-dimensional input per latent frame;
+ * in each double-stream block, following its video MLP, the video tokens
+ * cross-attend to the projected camera features in chunks of one latent
+ * frame).
  *
  * Row r (0 <= r < n_tok) belongs to chunk c = r / tokens_per_chunk (e.g.
  * tokens_per_chunk = 880 for one 22x40 latent frame) and attends to camera

@@ -1,15 +1,13 @@
 """Segment-wise causal joint attention over a KV cache plus the current segment.
 
 Source: "Hy-Nomas: Towards Free-Form Interactive World Generation", section
-"Segment-Autoregressive Diffusion Transformer": text and video tokens interact
-through segment-wise causal joint attention; the layer's KV cache supplies
-context from earlier segments; the current segment attends to all past KV
-cache and the current conditioning; attention is causal across segments (no
-future segment is needed); cached keys and values are reused when generation
-advances. Architecture table: 16 heads of 128 dimensions. "Hy-Nomas Explained
-...", Step 2 "Segment-wise causal joint attention": current-segment tokens
-attend to the current segment and to everything cached from earlier segments,
-never to later ones.
+"Segment-Autoregressive Diffusion Transformer": one joint attention mixes the
+text and video tokens of a block; each layer keeps the keys and values of the
+segments already generated and reuses them; a segment's tokens see the
+earlier segments (through that cache) and their own segment, and never a
+later one. Architecture table: 16 heads of 128 dimensions. "Hy-Nomas Explained
+...", Step 2 "Segment-wise causal joint attention": the same visibility rule,
+earlier and current segments only.
 
 The method computes exactly (up to rounding order) masked softmax attention,
 so this is that definition in float64:

@@ -1,11 +1,11 @@
 """Per-latent-frame camera cross-attention.
 
-Source: model card, section "Text and Camera Conditioning" (camera
-extrinsics grouped over four video frames into 64-dimensional inputs, one per
-latent frame; at every double-stream block the video tokens query the
-projected camera features through cross-attention after the video MLP; with
-per-chunk camera attention and a chunk size of one, the attention is aligned
-to individual latent frames) and the Explainer's camera-conditioning section.
+Source: model card, section "Text and Camera Conditioning" (the camera
+extrinsics of four video frames form one 64-dimensional input per latent
+frame; in each double-stream block, following its video MLP, the video tokens
+cross-attend to the projected camera features, chunk by chunk, and a chunk of
+one latent frame ties each frame's tokens to that frame's camera) and the
+Explainer's camera-conditioning section.
 
 Reading: video rows are grouped into chunks of `tokens_per_chunk` consecutive
 rows (the latent frames of one camera chunk, raster order); chunk c owns

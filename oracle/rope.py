@@ -1,8 +1,8 @@
 """3D rotary position embedding on video tokens, in float64.
 
 Source: "Hy-Nomas: Towards Free-Form Interactive World Generation",
-architecture table row "Position encoding" (3D RoPE, temporal/height/width
-dimensions [16, 56, 56], theta 256) and section "Segment-Autoregressive
+architecture table, position-encoding row (3D RoPE; 16, 56 and 56 of the
+128 dimensions for t, h and w; theta 256) and section "Segment-Autoregressive
 Diffusion Transformer" (3D RoPE encodes video positions); "Hy-Nomas Explained
 ...", Step 2 "Segment-wise causal joint attention" (RoPE rotates query and key
 vectors by position; reference [16], RoFormer).

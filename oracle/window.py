@@ -1,10 +1,9 @@
 """Bounded GPU history: which cached latent frames the attention reads.
 
 Source: "Hy-Nomas: Towards Free-Form Interactive World Generation", section
-"Segment-Autoregressive Diffusion Transformer" (the single-GPU configuration
-selects a bounded set of historical latent frames, default budget 18, which
-excludes the current segment; the standard configuration keeps the full
-history) and section "Single-GPU Low-Memory Inference" (up to 18 historical
+"Segment-Autoregressive Diffusion Transformer" (on one GPU only a limited
+number of past latent frames is attended, 18 by default and not counting the
+current segment; the standard configuration attends to the whole history) and section "Single-GPU Low-Memory Inference" (up to 18 historical
 frames chosen by temporal_context sampling, older ones archived on CPU);
 "Tencent Opens Hy-Nomas ...", section "How the RTX 4090 configuration saves
 memory" (a sliding, fixed context window bounds KV-cache growth).

@@ -2,8 +2,8 @@
 // quantising to INT8 for an INT8 cache.
 //
 // Source: "Hy-Nomas: Towards Free-Form Interactive World Generation", section
-// "Segment-Autoregressive Diffusion Transformer" (cached keys and values are
-// reused when generation advances) and section "Single-GPU Low-Memory
+// "Segment-Autoregressive Diffusion Transformer" (cached keys and values
+// serve again as generation moves on) and section "Single-GPU Low-Memory
 // Inference" (keys and values cached in INT8, attention kept in BF16).
 // Quantiser (this library's scheme, per token and head, K and V separately):
 //   scale = fp32(max|x| / 127)                       IEEE fp32 division

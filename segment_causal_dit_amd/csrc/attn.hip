@@ -2,9 +2,9 @@
 // segment(s), on gfx950 bf16 MFMA.
 //
 // Source: "Hy-Nomas: Towards Free-Form Interactive World Generation", section
-// "Segment-Autoregressive Diffusion Transformer" (text and video interact
-// through segment-wise causal joint attention; the layer's KV cache supplies
-// earlier segments; attention is causal across segments) and section
+// "Segment-Autoregressive Diffusion Transformer" (one joint attention over
+// text and video, causal across segments, with the layer's cache holding the
+// earlier segments) and section
 // "Single-GPU Low-Memory Inference" (INT8 KV storage, BF16 attention);
 // architecture table (16 heads x 128).
 //

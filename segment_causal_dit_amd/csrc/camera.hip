@@ -3,10 +3,10 @@
 //
 // Source: "Hy-Nomas: Towards Free-Form Interactive World Generation" (model
 // card), section "Text and Camera Conditioning": camera extrinsics become one
-// 64-dimensional input per latent frame; at every double-stream block the
-// video tokens query the projected camera features through cross-attention
-// after the video MLP; with per-chunk camera attention and a chunk size of
-// one the attention is aligned to individual latent frames.
+// 64-dimensional input per latent frame; in each double-stream block, following
+// its video MLP, the video tokens cross-attend to the projected camera
+// features chunk by chunk, and a one-frame chunk ties each latent frame's
+// tokens to its own camera.
 //
 // Row r (of n_tok video rows) is in chunk c = r / tokens_per_chunk, whose
 // camera tokens are rows [c t_cam, (c + 1) t_cam) of k and v. Per head:

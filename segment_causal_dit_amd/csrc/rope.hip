@@ -1,8 +1,8 @@
 // 3D rotary position embedding of video rows, bf16 in and out.
 //
 // Source: "Hy-Nomas: Towards Free-Form Interactive World Generation",
-// architecture table row "Position encoding" (3D RoPE, temporal/height/width
-// dimensions [16, 56, 56], theta 256) and section "Segment-Autoregressive
+// architecture table, position-encoding row (3D RoPE; 16, 56 and 56 of the
+// 128 dimensions for t, h and w; theta 256) and section "Segment-Autoregressive
 // Diffusion Transformer" (RoPE encodes video positions). Pair (2i, 2i+1) of a
 // slice of width d is rotated by pos_axis * theta^(-2i/d); with even slice
 // widths the pair index is simply element / 2 across the whole head.
