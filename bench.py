@@ -785,6 +785,23 @@ def main():
            app_bytes / (app_ms * 1e-3) / 1e9 if app_ms else 0, ms_step))
     if expand:
         log("window dequant %.3f ms (%.0f GB/s)" % (deq_ms, deq_bytes / (deq_ms * 1e-3) / 1e9))
+        # beside it: the same attention over the INT8 cache itself, the dequantisation fused into the
+        # tile loads (bit-identical output); reported, not part of the step
+        slots = sc.window_select(cache.slot_t[:n_hist_frames], cfg.window)
+        hist = torch.from_numpy(slots).to(dev)
+        fused = []
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sc.segcausal_joint_attn(q, k, v, [(0, tl, seg.text_valid)], cfg.sm_scale, cache=cache,
+                                    hist_slots=hist, out=out)
+            b.record(stream)
+            fused.append((a, b))
+        torch.cuda.synchronize()
+        fused_ms = float(np.mean([a.elapsed_time(b) for a, b in fused[1:]]))
+        fused_tflops = flops / (fused_ms * 1e-3) / 1e12
+        log("attention over the INT8 cache (dequantisation in the tile loads) %.3f ms (%.1f TFLOP/s)"
+            % (fused_ms, fused_tflops))
 
     traffic = measured_traffic(cfg, history_path(cfg, args.int8_attn))
     line = {
@@ -822,6 +839,9 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if expand:
+        line["int8_cache_attention"] = {"ms": round(fused_ms, 4), "tflops": round(fused_tflops, 3),
+                                        "frac": round(fused_tflops / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         del q_pre, k_pre, q, k, v, out, cache, win
