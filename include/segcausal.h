@@ -251,7 +251,8 @@ typedef struct segc_camera_args {
 
 /*
  * Errors: EINVAL on null/misaligned pointers (q only when t_cam > 1), n_tok
- *   outside [0, 2^31), n_heads outside [1, 1024], tokens_per_chunk < 1, t_cam
+ *   outside [0, 2^31), n_heads outside [1, 1024], n_tok x n_heads >= 2^31
+ *   (the launch grid and row indexes are 32-bit), tokens_per_chunk < 1, t_cam
  *   outside [1, 4096], bad strides, sm_scale <= 0 or not finite, o equal to
  *   q, k or v; EUNSUPPORTED if head_dim != 128. n_tok == 0 is a no-op.
  */
@@ -319,7 +320,9 @@ typedef struct segc_attn_args {
 } segc_attn_args;
 
 /*
- * Errors: EINVAL on null/misaligned pointers, n_cur < 0, bad strides, bad
+ * Errors: EINVAL on null/misaligned pointers, n_cur < 0 or > 2^30,
+ *   n_heads outside [1, 1024], n_cur x n_heads >= 2^31 (the launch grid and
+ *   row indexes are 32-bit), bad strides, bad
  *   segment tables (not starting at 0, not ascending, not ending at n_cur,
  *   text_valid > text_len, text_len longer than its segment), a segment whose
  *   queries would see no key, n_hist < 0 or > n_slots, n_hist > 0 without a
@@ -379,7 +382,8 @@ typedef struct segc_attn_bwd_args {
 
 /*
  * Errors: EINVAL on null/misaligned pointers (rows 16-byte aligned, lse and
- *   delta 4-byte aligned), n < 0 or n >= 2^30, bad strides, bad segment
+ *   delta 4-byte aligned), n < 0 or n >= 2^30, n x n_heads >= 2^31 (the
+ *   launch grid and row indexes are 32-bit), bad strides, bad segment
  *   tables (as for segcausal_joint_attn, including a segment whose queries
  *   would see no key), sm_scale <= 0 or not finite, an output (dq, dk, dv,
  *   delta) whose base pointer equals another argument's (in-place);

@@ -338,6 +338,7 @@ int camera_cross_attn(const segc_camera_args* a, void* stream) {
   if (a->head_dim != SEGC_HEAD_DIM) return fail(SEGC_EUNSUPPORTED, "head_dim %d != 128", a->head_dim);
   if (a->n_tok < 0 || a->n_tok >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "n_tok out of range");
   if (a->n_heads < 1 || a->n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  if (a->n_tok * a->n_heads >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "n_tok x n_heads must be below 2^31");
   if (a->tokens_per_chunk < 1) return fail(SEGC_EINVAL, "tokens_per_chunk must be >= 1");
   if (a->t_cam < 1 || a->t_cam > 4096) return fail(SEGC_EINVAL, "t_cam must be in [1, 4096]");
   if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
@@ -399,6 +400,8 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
     return fail(SEGC_EUNSUPPORTED, "n_seg %d outside [1, %d]", a->n_seg, SEGC_MAX_SEG);
   if (a->n_cur < 0 || a->n_cur > (int64_t)1 << 30) return fail(SEGC_EINVAL, "n_cur out of range");
   if (a->n_heads < 1 || a->n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  // (row, head) pairs index the launch grid and the kernels' 32-bit row math
+  if (a->n_cur * a->n_heads >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "n_cur x n_heads must be below 2^31");
   if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
     return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
   if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->k_stride_tok, a->k_stride_head) ||
@@ -481,6 +484,7 @@ int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
     return fail(SEGC_EUNSUPPORTED, "n_seg %d outside [1, %d]", a->n_seg, SEGC_MAX_SEG);
   if (a->n < 0 || a->n >= (int64_t)1 << 30) return fail(SEGC_EINVAL, "n out of range");
   if (a->n_heads < 1 || a->n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
+  if (a->n * a->n_heads >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "n x n_heads must be below 2^31");
   if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
     return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
   const int64_t st[8][2] = {{a->q_stride_tok, a->q_stride_head},   {a->k_stride_tok, a->k_stride_head},

@@ -400,3 +400,15 @@ def test_binding_argtypes_match_header_arity():
         n_params = 0 if params in ("", "void") else params.count(",") + 1
         argtypes = getattr(lib, name).argtypes
         assert len(argtypes or []) == n_params, (name, n_params, argtypes)
+
+
+@pytest.mark.parametrize("call", [
+    lambda: _attn(n_cur=1 << 30, n_heads=2),        # 2^31 (row, head) pairs
+    lambda: _attn(n_cur=(1 << 28) + 1, n_heads=8),
+    lambda: _attn_bwd(n=1 << 29, n_heads=4),
+    lambda: _cam(n_tok=1 << 28, n_heads=8),
+])
+def test_pair_count_beyond_32_bit_grid_rejected(call):
+    # every size is inside its own range; the product of rows and heads is not
+    assert call() == 1
+    assert "2^31" in lib.segcausal_last_error().decode()
