@@ -506,6 +506,14 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb, o[db], 0, 0, 0);
     }
   }
+  // V^T reads two products ahead of their use
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   // use the sum here: otherwise its adds sink below the staging branch that
   // follows and run, with no products left to hide them, before the barrier
   asm volatile("" :: "v"(ls));
