@@ -11,12 +11,16 @@
 // with scale 0 and all-zero codes for an all-zero row.
 //
 // x / scale + 128 (the biased code before rounding) is first estimated as
-// fma(x, rcp(scale), 128) with the hardware reciprocal (within 1 ulp): the
-// estimate is within 3.4e-5 of the exact value and the IEEE quotient within
-// 2^-18 of x / scale (|x / scale| <= 127), so unless the estimate lies
-// within 2^-14 of a half-integer both round to the same integer; otherwise
-// the IEEE division decides (an all-zero row, rcp 0, gives codes 0). The
-// division runs in a wave-uniform branch, taken by about one wave in eight.
+// fma(x, rcp(scale), 128) with the hardware reciprocal (within 1 ulp for a
+// normal scale): the estimate is within 3.4e-5 of the exact value and the
+// IEEE quotient within 2^-18 of x / scale (|x / scale| <= 127), so unless the
+// estimate lies within 2^-14 of a half-integer both round to the same
+// integer; otherwise the IEEE division decides (an all-zero row, rcp 0, gives
+// codes 0). A row whose scale is subnormal (absmax below 127 * 2^-126; bf16
+// inputs reach down to 2^-133) has no usable reciprocal (it loses accuracy,
+// and overflows to infinity below 2^-128), so every element of such a row
+// takes the IEEE division. The division runs in a wave-uniform branch, taken
+// by about one wave in eight on unit-scale data.
 //
 // Layout: a workgroup of 256 lanes handles 16 consecutive tokens of one head;
 // 16 lanes per (token, head), 8 elements each. HBM-bound: 776 B per
@@ -60,23 +64,29 @@ __device__ inline u32x2 quant_row8(const u32x4 in, float* scale_out) {
   a = row16_max(a);
   const float scale = a / 127.0f;                    // IEEE fp32 division
   *scale_out = scale;
-  const float rcp = scale != 0.0f ? __builtin_amdgcn_rcpf(scale) : 0.0f;   // all-zero row: codes 0
-  // |x / scale| <= 127 (1 + 2^-24) < 127.5 since scale = fp32(max|x| / 127),
-  // so the biased code rint(x / scale) + 128 lies in [1, 255]. Its estimate
-  // v = fma(x, rcp, 128) (one rounding) is within 3.4e-5 of the exact
+  // a subnormal scale: the whole row is divided (same value in all 16 lanes)
+  const bool tiny = scale != 0.0f && scale < 0x1p-126f;
+  // all-zero row: rcp 0, codes 0
+  const float rcp = (scale != 0.0f && !tiny) ? __builtin_amdgcn_rcpf(scale) : 0.0f;
+  // |x / scale| <= 127 (1 + 2^-24) < 127.5 for a normal scale = fp32(max|x| /
+  // 127), so the biased code rint(x / scale) + 128 lies in [1, 255]. Its
+  // estimate v = fma(x, rcp, 128) (one rounding) is within 3.4e-5 of the exact
   // x / scale + 128; away from ties (2^-14) the byte conversion's own
   // round-to-nearest-even of v gives the biased code.
   float v[8];
-  bool near = false;
+  bool near = tiny;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     v[i] = fmaf(x[i], rcp, 128.0f);
     near |= fabsf(v[i] - rintf(v[i])) >= 0.5f - 0x1p-14f;
   }
   if (__builtin_amdgcn_ballot_w64(near)) {
+    // (a subnormal scale carries a relative error up to 2^-10, so the clamp
+    // to +-127 is kept explicitly here; the biased byte never reaches 0)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (fabsf(v[i] - rintf(v[i])) >= 0.5f - 0x1p-14f) v[i] = rintf(x[i] / scale) + 128.0f;
+      if (tiny || fabsf(v[i] - rintf(v[i])) >= 0.5f - 0x1p-14f)
+        v[i] = fminf(fmaxf(rintf(x[i] / scale), -127.0f), 127.0f) + 128.0f;
   }
   // biased byte written in place, then XOR 0x80 per byte gives the
   // two's-complement code

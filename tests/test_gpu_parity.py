@@ -173,6 +173,57 @@ def test_append_random_shapes(i):
             assert np.array_equal(bits(cache.v[slot]), vf)
 
 
+def _tiny_rows(n_rows, seed):
+    """bf16 rows whose absmax spans 2^-133 .. 2^-100 (subnormal and normal
+    fp32 scales on either side of 2^-126), with zeros and near-ties inside:
+    the adversarial rows scaled by powers of two, then rounded to bf16 (which
+    keeps only the bits a subnormal bf16 value can hold)."""
+    rng = np.random.default_rng(seed)
+    x = oracle.bf16_bits_to_f64(_adversarial_rows(n_rows, seed))
+    a = np.abs(x).max(axis=1)
+    a[a == 0] = 1.0
+    e = rng.integers(-133, -99, size=n_rows)
+    x = x * np.exp2(e - np.floor(np.log2(a)))[:, None]      # absmax in [2^e, 2^(e+1))
+    x[rng.random(x.shape) < 0.1] = 0.0
+    # rows with absmax exactly at, and one bf16 step below, 127 * 2^-126 (scale
+    # 2^-126, then the largest subnormal scales), and the advisor-style row
+    # [a, a/2, -a/4, 0] at a = 2^-122, 2^-126, 2^-130
+    edge = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(np.array([127.0 * 2.0 ** -126])))[0]
+    below = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(np.array([edge])) - 1)[0]
+    for i, amax in enumerate([edge, below, 2.0 ** -122, 2.0 ** -126, 2.0 ** -130]):
+        x[2 + i] = np.linspace(-amax, amax, HEAD_DIM) * 0.9
+        x[2 + i, :4] = [amax, amax / 2, -amax / 4, 0.0]
+    return oracle.f64_to_bf16_bits(x)
+
+
+def test_append_tiny_rows_bit_exact():
+    # rows whose fp32 scale is subnormal take the IEEE division for every
+    # element; codes stay in [-127, 127] and equal the oracle's bit for bit, and
+    # the window expansion of those frames equals bf16(fp32(code * scale))
+    g, h, nf = 48, 2, 3
+    rows = _tiny_rows(nf * g * h, 81).reshape(nf * g, h, HEAD_DIM)
+    vrows = _tiny_rows(nf * g * h, 82).reshape(nf * g, h, HEAD_DIM)
+    kf = oracle.bf16_bits_to_f64(rows)
+    assert np.abs(kf).max(axis=-1).min() < 2.0 ** -126 * 127, "no subnormal-scale rows drawn"
+    cache = sc.KVCache(nf + 1, h, g, "int8", "cuda")
+    sc.kv_cache_append(cache, 1, _bf(rows), _bf(vrows))
+    torch.cuda.synchronize()
+    for f in range(nf):
+        for got_c, got_s, src in ((cache.k, cache.k_scale, rows), (cache.v, cache.v_scale, vrows)):
+            fr = oracle.bf16_bits_to_f64(src[f * g:(f + 1) * g]).transpose(1, 0, 2)
+            c, s = oracle.quantise_int8(fr)
+            gc = got_c[1 + f].cpu().numpy()
+            assert gc.min() >= -127, "code -128 emitted"
+            assert np.array_equal(gc, c), "frame %d: %d codes differ" % (f, (gc != c).sum())
+            assert np.array_equal(got_s[1 + f].cpu().numpy(), s)
+    win = _dequant_window(cache, [1, 2, 3])
+    for t in range(nf):
+        for got, codes, scales in ((win.k, cache.k, cache.k_scale), (win.v, cache.v, cache.v_scale)):
+            exp = oracle.f64_to_bf16_bits(oracle.dequantise_int8_bf16(codes[1 + t].cpu().numpy(),
+                                                                     scales[1 + t].cpu().numpy()))
+            assert np.array_equal(bits(got[t]), exp), t
+
+
 # ------------------------------------------------------------- attention ----
 
 def _check_chain(name):
