@@ -18,8 +18,9 @@
  *    The library never allocates, frees or keeps pointers after returning.
  *  - bf16 tensors of rows are laid out [rows][heads][128] with the 128 head
  *    elements contiguous; the token and head strides are given in ELEMENTS and
- *    must be multiples of 8 (16-byte aligned rows); base pointers must be
- *    16-byte aligned.
+ *    must be multiples of 8 (16-byte aligned rows) below SEGC_MAX_STRIDE
+ *    (the kernels form a row's offset inside a staged group of rows in 32
+ *    bits); base pointers must be 16-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call is asynchronous on that stream; the library never
  *    synchronises. The caller keeps buffers alive until the stream has run the
@@ -52,6 +53,7 @@ extern "C" {
 
 #define SEGC_HEAD_DIM 128    /* 16 heads x 128 dims per head (model card, architecture table) */
 #define SEGC_MAX_SEG  16     /* packed segments per attention call */
+#define SEGC_MAX_STRIDE ((int64_t)1 << 26)   /* exclusive bound on every stride, in elements */
 
 /*
  * A per-layer KV cache of latent frames (the keys and values of earlier
@@ -207,7 +209,7 @@ int kv_archive_store(const segc_cache* cache, const int32_t* slots, const segc_c
  *           overwritten; it may not overlap x, w or y
  * Errors: EINVAL on m outside [0, 2^31), negative n or k, ldx < k or not a
  *   multiple of 8, ldw < k or not a multiple of 16, ldy < n or not a
- *   multiple of 4, NULL or misaligned pointers (x, w, w_scale, bias,
+ *   multiple of 4, ldx, ldw or ldy at or above SEGC_MAX_STRIDE, NULL or misaligned pointers (x, w, w_scale, bias,
  *   workspace: 16 bytes; y: 8 bytes), y equal to x or w, a workspace
  *   overlapping x, w or y; EUNSUPPORTED unless n is a multiple of 256 and k
  *   a positive multiple of 64. m == 0 or n == 0 is a no-op.
@@ -327,7 +329,8 @@ typedef struct segc_attn_args {
  *   text_valid > text_len, text_len longer than its segment), a segment whose
  *   queries would see no key, n_hist < 0 or > n_slots, n_hist > 0 without a
  *   cache, a cache with n_heads different from the call's, sm_scale <= 0 or
- *   not finite; EUNSUPPORTED if head_dim != 128 or n_seg outside
+ *   not finite, a hist_slots pointer that is NULL (n_hist > 0) or not 4-byte
+ *   aligned; EUNSUPPORTED if head_dim != 128 or n_seg outside
  *   [1, SEGC_MAX_SEG]. n_cur == 0 is a no-op. Slot indices in hist_slots are
  *   read on the device and must lie in [0, n_slots) (a precondition).
  */
@@ -399,7 +402,7 @@ const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 6)
+#define SEGC_ABI_VERSION ((1 << 16) | 7)
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsegcausal.so")
+# SEGCAUSAL_LIB names another build of the same library (e.g. one with
+# host-side sanitizers); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("SEGCAUSAL_LIB") or os.path.join(_HERE, "libsegcausal.so")
 
 SEGC_OK, SEGC_EINVAL, SEGC_EUNSUPPORTED, SEGC_EHIP = 0, 1, 2, 3
 SEGC_BF16, SEGC_INT8 = 0, 1
@@ -117,6 +119,17 @@ def _rows(t, name):
     return t.data_ptr(), t.stride(0), t.stride(1)
 
 
+def _on_gpu(dev, **named):
+    """Every named tensor (None skipped) must live on GPU device `dev`: the
+    library receives bare pointers, and a host pointer or another device's
+    memory handed to a kernel faults the GPU."""
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU, got %s" % dev)
+    for name, t in named.items():
+        if t is not None and t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+
+
 def abi_version():
     return _lib.segcausal_abi_version()
 
@@ -131,6 +144,7 @@ def rope3d_apply(x_in, pos, x_out=None, theta=256.0, dims=(16, 56, 56), stream=N
         raise ValueError("x_in and x_out must share shape and strides")
     if pos.dtype != torch.int32 or not pos.is_contiguous() or tuple(pos.shape) != (x_in.shape[0], 3):
         raise ValueError("pos must be contiguous int32 [rows, 3]")
+    _on_gpu(x_in.device, x_out=x_out, pos=pos)
     _check(_lib.rope3d_apply(pi, po, x_in.shape[0], x_in.shape[1], HEAD_DIM, st, sh,
                              pos.data_ptr(), float(theta), dims[0], dims[1], dims[2],
                              _stream(stream)))
@@ -186,6 +200,9 @@ def kv_cache_append(cache, first_slot, k, v, t_first=None, stream=None):
     g = cache.tokens_per_frame
     if k.shape[0] != v.shape[0] or k.shape[0] % g:
         raise ValueError("k and v must hold the same whole number of frames")
+    if k.shape[1] != cache.desc.n_heads or v.shape[1] != cache.desc.n_heads:
+        raise ValueError("k and v must have the cache's %d heads" % cache.desc.n_heads)
+    _on_gpu(cache.k.device, k=k, v=v)
     n_frames = k.shape[0] // g
     _check(_lib.kv_cache_append(ctypes.byref(cache.desc), first_slot, n_frames,
                                 pk, kst, ksh, pv, vst, vsh, _stream(stream)))
@@ -201,6 +218,7 @@ def kv_window_dequant(cache, slots, out, stream=None):
     window then reads `out` with hist_slots = 0, 1, ... ."""
     if slots.dtype != torch.int32 or slots.dim() != 1 or not slots.is_contiguous():
         raise ValueError("slots must be a contiguous 1-D int32 tensor")
+    _on_gpu(cache.k.device, slots=slots, out=out.k)
     _check(_lib.kv_window_dequant(ctypes.byref(cache.desc), slots.data_ptr(), slots.shape[0],
                                   ctypes.byref(out.desc), _stream(stream)))
     return slots.shape[0]
@@ -259,6 +277,7 @@ def w8a16_linear(x, w_codes, w_scale, bias=None, out=None, workspace=None, strea
         workspace = torch.empty(n * k, dtype=torch.bfloat16, device=x.device)
     if workspace.dtype != torch.bfloat16 or not workspace.is_contiguous() or workspace.numel() < n * k:
         raise ValueError("workspace must be a contiguous bf16 tensor of >= n * k elements")
+    _on_gpu(x.device, w_codes=w_codes, w_scale=w_scale, bias=bias, out=out, workspace=workspace)
     _check(_lib.w8a16_linear(x.data_ptr(), x.stride(0), w_codes.data_ptr(), w_codes.stride(0),
                              w_scale.data_ptr(), bias.data_ptr() if bias is not None else None,
                              out.data_ptr(), out.stride(0), m, n, k, workspace.data_ptr(), _stream(stream)))
@@ -275,8 +294,13 @@ def camera_cross_attn(q, k_cam, v_cam, tokens_per_chunk, sm_scale, out=None, str
     t_cam = k_cam.shape[0] // n_chunks
     if k_cam.shape != v_cam.shape or k_cam.stride() != v_cam.stride():
         raise ValueError("k_cam and v_cam must share shape and strides")
+    if k_cam.dim() != 3 or k_cam.shape[1] != nh:
+        raise ValueError("k_cam and v_cam must be [rows, %d, 128] like q" % nh)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if tuple(out.shape[:2]) != (n, nh):
+        raise ValueError("out must be [%d, %d, 128] like q" % (n, nh))
+    _on_gpu(q.device, k_cam=k_cam, v_cam=v_cam, out=out)
     pq, qst, qsh = _rows(q, "q")
     pk, kst, ksh = _rows(k_cam, "k_cam")
     pv, _, _ = _rows(v_cam, "v_cam")
@@ -313,6 +337,13 @@ def segcausal_joint_attn(q, k, v, segments, sm_scale, cache=None, hist_slots=Non
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     po, ost, osh = _rows(out, "out")
     n_cur, nh = q.shape[0], q.shape[1]
+    for t, nm in ((k, "k"), (v, "v"), (out, "out")):
+        if tuple(t.shape[:2]) != (n_cur, nh):
+            raise ValueError("%s must be [%d, %d, 128] like q" % (nm, n_cur, nh))
+    if hist_slots is not None and hist_slots.numel() > 0 and cache is None:
+        raise ValueError("hist_slots needs a cache")
+    _on_gpu(q.device, k=k, v=v, out=out, lse=lse, hist_slots=hist_slots,
+            cache=cache.k if cache is not None else None)
     seg_start, tl, tv = _segment_tables(segments, n_cur)
     n_hist = 0
     hs_ptr = None
@@ -367,6 +398,7 @@ def segcausal_joint_attn_bwd(q, k, v, o, dout, lse, segments, sm_scale, dq=None,
     for t, nm in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
         if tuple(t.shape[:2]) != (n, nh):
             raise ValueError("%s must be [%d, %d, 128] like q" % (nm, n, nh))
+    _on_gpu(q.device, k=k, v=v, o=o, dout=dout, dq=dq, dk=dk, dv=dv, lse=lse, delta=delta)
     strides = [x for r in rows for x in r[1:]]
     seg_start, tl, tv = _segment_tables(segments, n)
     args = SegcAttnBwdArgs(*([r[0] for r in rows] + strides +

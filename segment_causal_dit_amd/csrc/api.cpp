@@ -34,8 +34,11 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Strides are multiples of 8 elements (16-byte rows) and below
+// SEGC_MAX_STRIDE: the kernels form a row's offset inside a staged group of at
+// most 16 rows in 32 bits (15 * 2 bytes * 2^26 < 2^31).
 bool strides_ok(int64_t st, int64_t sh) {
-  return st >= 0 && sh >= 0 && st % 8 == 0 && sh % 8 == 0;
+  return st >= 0 && sh >= 0 && st % 8 == 0 && sh % 8 == 0 && st < SEGC_MAX_STRIDE && sh < SEGC_MAX_STRIDE;
 }
 
 // Segment tables: rows [seg_start[s], seg_start[s+1]) are segment s, its first
@@ -183,7 +186,7 @@ int rope3d_apply(const void* x_in, void* x_out, int64_t n_tok, int32_t n_heads, 
   if (n_heads < 1 || n_heads > 1024) return fail(SEGC_EINVAL, "n_heads out of range");
   if (!(theta > 0.0) || !std::isfinite(theta)) return fail(SEGC_EINVAL, "theta must be > 0");
   if (!strides_ok(stride_tok, stride_head))
-    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements below 2^26");
   if (n_tok == 0) return ok();
   if (!x_in || !x_out || !pos) return fail(SEGC_EINVAL, "NULL pointer");
   if (!aligned16(x_in) || !aligned16(x_out))
@@ -218,7 +221,7 @@ int kv_cache_append(const segc_cache* cache, int32_t first_slot, int32_t n_frame
   if (n_frames < 0 || n_frames > cache->n_slots)
     return fail(SEGC_EINVAL, "n_frames %d outside [0, n_slots=%d]", n_frames, cache->n_slots);
   if (!strides_ok(k_stride_tok, k_stride_head) || !strides_ok(v_stride_tok, v_stride_head))
-    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements below 2^26");
   const int64_t n_tok = (int64_t)n_frames * cache->tokens_per_frame;
   if (n_tok > (int64_t)1 << 30) return fail(SEGC_EINVAL, "append too large");
   if (n_frames == 0) return ok();
@@ -296,6 +299,9 @@ int w8a16_linear(const void* x, int64_t ldx, const int8_t* w, int64_t ldw, const
   if (ldx < k || ldx % 8) return fail(SEGC_EINVAL, "ldx must be >= k and a multiple of 8");
   if (ldw < k || ldw % 16) return fail(SEGC_EINVAL, "ldw must be >= k and a multiple of 16");
   if (ldy < n || ldy % 4) return fail(SEGC_EINVAL, "ldy must be >= n and a multiple of 4");
+  // row offsets inside a staged group (up to 8 rows) are formed in 32 bits
+  if (ldx >= SEGC_MAX_STRIDE || ldw >= SEGC_MAX_STRIDE || ldy >= SEGC_MAX_STRIDE)
+    return fail(SEGC_EINVAL, "ldx, ldw and ldy must be below 2^26");
   if (m == 0 || n == 0) return ok();
   if (!x || !w || !w_scale || !y || !workspace) return fail(SEGC_EINVAL, "NULL x/w/w_scale/y/workspace");
   if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & 7u) || !aligned16(w_scale) ||
@@ -345,7 +351,7 @@ int camera_cross_attn(const segc_camera_args* a, void* stream) {
     return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
   if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->kv_stride_tok, a->kv_stride_head) ||
       !strides_ok(a->o_stride_tok, a->o_stride_head))
-    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements below 2^26");
   if (a->n_tok == 0) return ok();
   if (!a->k || !a->v || !a->o || (a->t_cam > 1 && !a->q)) return fail(SEGC_EINVAL, "NULL q/k/v/o");
   if ((a->q && !aligned16(a->q)) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
@@ -406,7 +412,7 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
     return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
   if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->k_stride_tok, a->k_stride_head) ||
       !strides_ok(a->v_stride_tok, a->v_stride_head) || !strides_ok(a->o_stride_tok, a->o_stride_head))
-    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+    return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements below 2^26");
   int rc = check_segments(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, a->n_cur);
   if (rc) return rc;
   if (a->n_hist < 0) return fail(SEGC_EINVAL, "n_hist < 0");
@@ -421,6 +427,7 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
     if (a->n_hist > a->cache->n_slots)
       return fail(SEGC_EINVAL, "n_hist %d > n_slots %d", a->n_hist, a->cache->n_slots);
     if (!a->hist_slots) return fail(SEGC_EINVAL, "NULL hist_slots");
+    if ((uintptr_t)a->hist_slots & 3u) return fail(SEGC_EINVAL, "hist_slots must be 4-byte aligned");
     n_hist_rows = (int64_t)a->n_hist * a->cache->tokens_per_frame;
     if (n_hist_rows > (int64_t)1 << 30) return fail(SEGC_EINVAL, "history too long");
     hist_int8 = a->cache->dtype == SEGC_INT8;
@@ -493,7 +500,7 @@ int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
                             {a->dk_stride_tok, a->dk_stride_head}, {a->dv_stride_tok, a->dv_stride_head}};
   for (int i = 0; i < 8; ++i)
     if (!strides_ok(st[i][0], st[i][1]))
-      return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements");
+      return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements below 2^26");
   int rc = check_segments(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, a->n);
   if (rc) return rc;
   rc = check_visible(a->n_seg, a->seg_start, a->seg_text_len, a->seg_text_valid, 0);

@@ -60,6 +60,7 @@
 //  * workgroup ids are remapped so that each XCD (dispatched round-robin)
 //    works through contiguous query tiles of the same head, sharing K/V in L2.
 #include "internal.h"
+#include "lds_dma.h"
 #include "segtab.h"
 
 namespace segc {
@@ -227,44 +228,6 @@ __device__ inline int64_t hist_row_generic(const AttnParams& p, const Group& g, 
 __device__ inline int k_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 __device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ (5 * (r & 3))) << 4); }
 
-// Direct global -> LDS copies: lane l's bytes land at lds_base + size * l
-// (lds_base is wave-uniform).
-// Issued from inline assembly: the compiler then records no pending LDS
-// write, so it does not drain these loads (s_waitcnt vmcnt(0)) before every
-// later LDS read of the other buffer. Completion is awaited explicitly
-// (stage_finish) before the barrier that publishes the tile. M0 holds the
-// LDS base; gfx9 needs one wait state between an SALU write of M0 and an
-// LDS-DMA load. Nothing else in this kernel keeps a value in M0.
-// A generic pointer into LDS holds the LDS byte address in its low 32 bits
-// (the shared aperture is 4 GB aligned; the address-space cast would add a
-// null check per use, which these never-null tile pointers do not need).
-__device__ inline uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-__device__ inline void dload16(const void* g, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
-}
-__device__ inline void dload4(const void* g, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(g), "s"(lds_addr(lds_base)) : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
-// offset (the load's scalar-base form: no per-lane 64-bit address math).
-__device__ inline void dload16_s(uint32_t voff, uint64_t sbase, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory", "m0");
-}
-// A kernel-argument pointer as a wave-uniform value (keeps a per-lane choice
-// between two such pointers a register select, not a per-lane load).
-__device__ inline uintptr_t uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  // readfirstlane yields int: widen each half as unsigned (no sign extension)
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-  return ((uint64_t)hi << 32) | (uint64_t)lo;
-}
-
 // Issue the loads of staging wave w's group of tile tl: bf16 rows go
 // straight into the K/V tiles of `buf`; INT8 history rows go into `raw`
 // (codes, plus the group's K and V scales) for stage_finish to convert.
@@ -280,12 +243,12 @@ __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, in
       uint64_t kb, vb;
       uint32_t ks, vs;
       if (tl.hist) {
-        kb = uniform_ptr((const char*)p.hk + g.row0 * 256);
-        vb = uniform_ptr((const char*)p.hv + g.row0 * 256);
+        kb = uniform_addr((const char*)p.hk + g.row0 * 256);
+        vb = uniform_addr((const char*)p.hv + g.row0 * 256);
         ks = vs = 256;
       } else {
-        kb = uniform_ptr(p.k + g.row0 * p.k_st + head * p.k_sh);
-        vb = uniform_ptr(p.v + g.row0 * p.v_st + head * p.v_sh);
+        kb = uniform_addr(p.k + g.row0 * p.k_st + head * p.k_sh);
+        vb = uniform_addr(p.v + g.row0 * p.v_st + head * p.v_sh);
         ks = (uint32_t)p.k_st * 2;
         vs = (uint32_t)p.v_st * 2;
       }
@@ -336,14 +299,14 @@ __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, in
     // scales: lanes [0, RW) K of the group's rows, [RW, 2 RW) V, the rest repeat
     const int slr = min(lane & (RW - 1), g.lim);
     const int64_t scr = g.generic ? hist_row_generic(p, g, slr, head) : g.row0 + slr;
-    const uintptr_t sbase = (lane & RW) ? uniform_ptr(p.hvs) : uniform_ptr(p.hks);
+    const uint64_t sbase = (lane & RW) ? uniform_addr(p.hvs) : uniform_addr(p.hks);
 #pragma unroll
     for (int e = 0; e < RW / 8; ++e) {                     // 8 rows of codes per instruction
       const int off = (lane & 7) * 16;
       dload16((const char*)p.hk + cr[e] * 128 + off, raw + RAW_KC + (RW * w + 8 * e) * 128);
       dload16((const char*)p.hv + cr[e] * 128 + off, raw + RAW_VC + (RW * w + 8 * e) * 128);
     }
-    dload4((const void*)(sbase + (uintptr_t)scr * 4), raw + RAW_S + w * 256);
+    dload4((const void*)(sbase + (uint64_t)scr * 4), raw + RAW_S + w * 256);
     return 2 * (RW / 8) + 1;
   }
 }

@@ -21,11 +21,14 @@
 //    SIMD); each wave keeps its 32 rows' q and do as MFMA B operands and
 //    walks the key tiles it can see: S^T = K Q^T, dP^T = V dO^T, then
 //    dQ^T += K^T dS^T with K^T from the transposing LDS read;
-//  * dK/dV: one workgroup = 4 waves = 128 keys of one head (one wave per
-//    SIMD, for the registers of two 128 x 32 accumulators); each wave keeps
-//    its 32 keys' k and v as B operands and walks the query tiles that can
-//    see them: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and
-//    dK^T += Q^T dS.
+//  * dK/dV: one workgroup = 8 waves = 128 keys of one head (two waves per
+//    SIMD); K and V of the 128 keys sit in LDS and are re-read as B
+//    operands, so that the two 128 x 32 fp32 accumulators of a wave fit
+//    beside them; wave w owns keys 32 (w mod 4) .. + 31 and query rows
+//    32 floor(w / 4) .. + 31 of every 64-row query tile, walks the query
+//    tiles that can see its keys: S = Q K^T, dP = dO V^T, then
+//    dV^T += dO^T P and dK^T += Q^T dS; the two waves of a key group add
+//    their partial dK and dV through LDS at the end.
 // 64-row tiles are staged through LDS, double buffered, by direct global->LDS
 // loads issued from inline assembly and awaited explicitly once per tile.
 // Chunk c of tile row r sits at c ^ (((r & 3) << 2) | ((r >> 2) & 3)): every
@@ -34,6 +37,7 @@
 // pairs in which every key is video of a segment no later than the first
 // query's segment are fully visible and skip the per-element mask.
 #include "internal.h"
+#include "lds_dma.h"
 #include "segtab.h"
 
 namespace segc {
@@ -76,33 +80,6 @@ __device__ inline bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, 
 __device__ inline int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ inline int t_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
 
-// Direct global -> LDS copy of 16 bytes per lane (lane l lands at
-// lds_base + 16 l), issued from inline assembly so that the compiler does not
-// drain it before unrelated LDS reads; M0 holds the LDS base (one wait state
-// after the SALU write). Nothing else in these kernels keeps a value in M0.
-// A generic pointer into LDS holds the LDS byte address in its low 32 bits
-// (the shared aperture is 4 GB aligned; the address-space cast would add a
-// null check per use, which these never-null tile pointers do not need).
-__device__ inline uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-__device__ inline void dload16(const void* g, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds_addr(lds_base))
-               : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
-// offset (the load's scalar-base form: no per-lane 64-bit address math).
-__device__ inline void dload16_s(uint32_t voff, uint64_t sbase, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory", "m0");
-}
-// A wave-uniform address as SGPRs.
-__device__ inline uint64_t uniform_addr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-  return ((uint64_t)hi << 32) | (uint64_t)lo;
-}
 __device__ inline void dload_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ inline int seg_of(const AttnBwdParams& p, int r) {

@@ -24,18 +24,15 @@
 //    workgroup per CU walks its tiles and starts the next tile's loads right
 //    behind the previous tile's stores.
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace segc {
 namespace {
 
 constexpr int TN = 256;                 // output channels per workgroup
 constexpr int TM = 256;                 // activation rows per workgroup
-#ifndef GEMM_TK
-#define GEMM_TK 64
-#define GEMM_NSTG 2
-#endif
-constexpr int TK = GEMM_TK;             // k per stage
-constexpr int NSTG = GEMM_NSTG;         // LDS stages (loads run NSTG - 1 ahead)
+constexpr int TK = 64;                  // k per stage
+constexpr int NSTG = 2;                 // LDS stages (loads run NSTG - 1 ahead)
 constexpr int NTH = 512;
 constexpr int CH = TK / 8;              // 16-byte chunks per tile row
 constexpr int ROWB = TK * 2;            // bytes per tile row
@@ -61,33 +58,6 @@ __device__ inline int g_off(int r, int c) { return r * ROWB + ((c ^ g_swz(r)) <<
 __device__ inline uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
-}
-
-// Direct global -> LDS copy of 16 bytes per lane (lane l lands at
-// lds_base + 16 l), from inline assembly so that the compiler does not drain
-// it before unrelated LDS reads; M0 holds the LDS base. Completion is awaited
-// explicitly with vmcnt.
-// (A generic pointer into LDS holds the LDS byte address in its low 32 bits:
-// the shared aperture is 4 GB aligned, and the address-space cast would add a
-// null check per use.)
-__device__ inline uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-__device__ inline void dload16(const void* g, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "s"(lds_addr(lds_base))
-               : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
-// offset (the load's scalar-base form: no per-lane 64-bit address math).
-__device__ inline void dload16_s(uint32_t voff, uint64_t sbase, const char* lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_addr(lds_base)) : "memory", "m0");
-}
-__device__ inline uint64_t uniform_addr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-  return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
 // Four signed codes (one dword) -> four bf16, exact.

@@ -412,3 +412,124 @@ def test_pair_count_beyond_32_bit_grid_rejected(call):
     # every size is inside its own range; the product of rows and heads is not
     assert call() == 1
     assert "2^31" in lib.segcausal_last_error().decode()
+
+
+# ------------------------------------------- binding shape/device checks ----
+
+def _bf16(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_attention_refuses_mismatched_rows_or_heads():
+    # the C ABI sees only pointers and strides: the binding is the one place
+    # that knows tensor extents, so k, v and out must match q's [n, H]
+    x = _bf16(4, 2, 128)
+    cases = [dict(k=x[:3]), dict(v=_bf16(4, 3, 128)), dict(out=x[:2]), dict(out=_bf16(4, 1, 128))]
+    for bad in cases:
+        a = dict(q=x, k=x, v=x, out=None)
+        a.update(bad)
+        with pytest.raises(ValueError, match="like q"):
+            sc.segcausal_joint_attn(a["q"], a["k"], a["v"], [(0, 0, 0)], 1.0, out=a["out"])
+
+
+def test_binding_refuses_host_tensors():
+    # a host pointer handed to a kernel would fault the GPU: refused before the call
+    import torch
+    x = _bf16(4, 2, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        sc.segcausal_joint_attn(x, x, x, [(0, 0, 0)], 1.0)
+    with pytest.raises(ValueError, match="GPU"):
+        sc.segcausal_joint_attn_bwd(x, x, x, x, x, torch.zeros(2, 4), [(0, 0, 0)], 0.088)
+    with pytest.raises(ValueError, match="GPU"):
+        sc.rope3d_apply(x, torch.zeros(4, 3, dtype=torch.int32))
+    cache = sc.KVCache(2, 2, 4, "int8", device="cpu")
+    with pytest.raises(ValueError, match="GPU"):
+        sc.kv_cache_append(cache, 0, x, x)
+    win = sc.KVCache(2, 2, 4, "bf16", device="cpu")
+    with pytest.raises(ValueError, match="GPU"):
+        sc.kv_window_dequant(cache, torch.zeros(2, dtype=torch.int32), win)
+    with pytest.raises(ValueError, match="GPU"):
+        sc.w8a16_linear(_bf16(4, 64), torch.zeros(256, 64, dtype=torch.int8), torch.ones(256))
+    with pytest.raises(ValueError, match="GPU"):
+        sc.camera_cross_attn(x, x[:1], x[:1], 4, 1.0)
+
+
+def test_binding_append_refuses_other_head_counts():
+    cache = sc.KVCache(2, 2, 4, "int8", device="cpu")
+    with pytest.raises(ValueError, match="heads"):
+        sc.kv_cache_append(cache, 0, _bf16(4, 3, 128), _bf16(4, 3, 128))
+    with pytest.raises(ValueError, match="heads"):
+        sc.kv_cache_append(cache, 0, _bf16(4, 2, 128), _bf16(4, 1, 128))
+
+
+def test_binding_camera_refuses_other_head_counts():
+    x = _bf16(8, 2, 128)
+    with pytest.raises(ValueError, match="like q"):
+        sc.camera_cross_attn(x, _bf16(2, 3, 128), _bf16(2, 3, 128), 4, 1.0)
+    with pytest.raises(ValueError, match="like q"):
+        sc.camera_cross_attn(x, x[:2], x[:2], 4, 1.0, out=_bf16(8, 1, 128))
+
+
+def test_binding_hist_slots_without_cache_refused():
+    import torch
+    x = _bf16(4, 2, 128)
+    with pytest.raises(ValueError, match="cache"):
+        sc.segcausal_joint_attn(x, x, x, [(0, 0, 0)], 1.0, hist_slots=torch.zeros(1, dtype=torch.int32))
+
+
+# --------------------------------------- 32-bit offsets, alignment, EHIP ----
+
+MAX_STRIDE = 1 << 26
+
+
+def test_header_stride_bound():
+    m = re.search(r"#define SEGC_MAX_STRIDE \(\(int64_t\)1 << (\d+)\)", open(HEADER).read())
+    assert m and (1 << int(m.group(1))) == MAX_STRIDE
+
+
+@pytest.mark.parametrize("call", [
+    lambda: _attn(k_stride_tok=MAX_STRIDE), lambda: _attn(v_stride_tok=MAX_STRIDE),
+    lambda: _attn(q_stride_head=MAX_STRIDE), lambda: _attn(o_stride_tok=MAX_STRIDE),
+    lambda: _attn_bwd(q_stride_tok=MAX_STRIDE), lambda: _attn_bwd(do_stride_tok=MAX_STRIDE),
+    lambda: _attn_bwd(k_stride_tok=MAX_STRIDE), lambda: _attn_bwd(dv_stride_head=MAX_STRIDE),
+    lambda: _rope(st=MAX_STRIDE), lambda: _append(kst=MAX_STRIDE), lambda: _append(ksh=MAX_STRIDE),
+    lambda: _cam(kv_stride_tok=MAX_STRIDE), lambda: _cam(o_stride_head=MAX_STRIDE),
+    lambda: _lin(ldx=MAX_STRIDE), lambda: _lin(ldw=MAX_STRIDE), lambda: _lin(ldy=MAX_STRIDE),
+])
+def test_strides_that_would_wrap_32_bit_offsets_rejected(call):
+    # the kernels form row offsets inside a staged group of up to 16 rows in
+    # 32 bits; 15 * 2 bytes * 2^26 stays below 2^31, 2^26 itself is refused
+    assert call() == sc.SEGC_EINVAL
+    assert "2^26" in lib.segcausal_last_error().decode()
+
+
+def test_attn_rejects_misaligned_hist_slots():
+    # the kernel reads the slot list with 4-byte scalar loads
+    assert _attn(n_hist=2, cache=_cache(n_heads=2), hist_slots=FAKE + 2) == sc.SEGC_EINVAL
+    assert "hist_slots" in lib.segcausal_last_error().decode()
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+@pytest.mark.skipif(_gpu_present(), reason="with a GPU these stand-in pointers would reach a kernel")
+def test_launch_without_a_device_reports_hip_error():
+    # well-formed calls (the largest accepted strides among them) pass every
+    # host check; with no device the launch fails and the status is SEGC_EHIP
+    # with HIP's own message
+    calls = [
+        lambda: _rope(st=MAX_STRIDE - 8, sh=MAX_STRIDE - 8),
+        lambda: _append(kst=MAX_STRIDE - 8),
+        lambda: _dequant(),
+        lambda: _attn(k_stride_tok=MAX_STRIDE - 8),
+        lambda: _attn_bwd(),
+        lambda: _lin(ldx=MAX_STRIDE - 8, ws=0x100000000000),   # x then spans 13 GB
+        lambda: _cam(),
+    ]
+    for call in calls:
+        assert call() == sc.SEGC_EHIP
+        msg = lib.segcausal_last_error().decode()
+        assert "launch" in msg and len(msg) > len("launch: ")
