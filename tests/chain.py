@@ -122,6 +122,44 @@ def bits(t):
     return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+# Attention bars. The stated tolerance for unit-variance inputs is absolute:
+# max |err| <= 1e-2, mean |err| <= 1e-3. At long contexts the output itself
+# shrinks (|o| ~ sqrt(e / keys): rms 2.9e-3 over 317,056 keys), so an absolute
+# mean bar of 1e-3 would pass a kernel that dropped a tenth of the keys. The
+# derived bar therefore also holds each (row, head) to its own size, the rms of
+# its 128 reference values. Error sources: every product p_j v_j carries the
+# bf16 rounding of p (relative 2^-9), dequantised INT8 keys and values carry
+# relative 2^-9 each, and the output is rounded to bf16 once; each shifts an
+# output element by a fraction of its row's rms that does not shrink with the
+# key count. Exact arithmetic with just these roundings, over c4's 253,440
+# INT8 history keys (test_parity_bars.py), errs by mean 2^-8.5 and max 2^-6.0
+# of the row rms; bars: mean 2^-7 and max 2^-4 (2.8x and 4x that), which one
+# missing 64-key tile of 3,960 already exceeds (mean 2^-6.4).
+MAX_ERR, MEAN_ERR = 1e-2, 1e-3
+REL_MAX, REL_MEAN = 2.0 ** -4, 2.0 ** -7
+
+
+class AttnErr:
+    """Absolute and row-relative error of an attention output against the oracle."""
+
+    def __init__(self, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        d = np.abs(got - ref)
+        rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
+        rel = d / np.maximum(rms, 1e-300)
+        self.max, self.mean = float(d.max()), float(d.mean())
+        self.rel_max, self.rel_mean = float(rel.max()), float(rel.mean())
+
+    def ok(self):
+        return (self.max <= MAX_ERR and self.mean <= MEAN_ERR
+                and self.rel_max <= REL_MAX and self.rel_mean <= REL_MEAN)
+
+    def __repr__(self):
+        return ("max %.3e mean %.3e | of row rms: max %.3e (2^%.1f) mean %.3e (2^%.1f)"
+                % (self.max, self.mean, self.rel_max, np.log2(max(self.rel_max, 1e-300)),
+                   self.rel_mean, np.log2(max(self.rel_mean, 1e-300))))
+
+
 def attn_errors(got, ref):
-    d = np.abs(got - ref)
-    return float(d.max()), float(d.mean())
+    return AttnErr(got, ref)

@@ -3,8 +3,11 @@ CPU oracle on the same seeded inputs.
 
 Bars: RoPE outputs, INT8 codes and scales and BF16 cache copies bit-exact;
 attention outputs max |err| <= 1e-2 and mean |err| <= 1e-3 (unit-variance
-inputs); lse max |err| <= 5e-3 (a derived bound: bf16 rounding of P and of
-dequantised keys perturbs the logits by far less than this at these sizes).
+inputs) and, per (row, head), max <= 2^-4 and mean <= 2^-7 of the reference
+row's rms (derived in chain.py: the absolute bar alone stops binding at long
+contexts, where the output shrinks); lse max |err| <= 5e-3 (a derived bound:
+bf16 rounding of P and of dequantised keys perturbs the logits by far less
+than this at these sizes).
 """
 
 import sys
@@ -24,7 +27,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 sc = pytest.importorskip("segment_causal_dit_amd._lib")
 
-MAX_ERR, MEAN_ERR, LSE_ERR = 1e-2, 1e-3, 5e-3
+LSE_ERR = 5e-3
 SMALL = ["c0", "c0_int8", "c0_win3", "c0_pad", "c0_packed3",
          "mid_int8", "mid_bf16", "mid_packed", "mid_nocache", "max_seg16"]
 
@@ -248,10 +251,10 @@ def _check_chain(name):
             assert np.array_equal(bits(r.cache.k[:nf]), oracle.f64_to_bf16_bits(cache[0]))
         assert list(r.slots) == list(oracle.window_select(inp.slot_t, cfg.window))
     o_ref, lse_ref = oracle_chain(inp, cache=cache)
-    mx, mean = attn_errors(to_f64(r.o), o_ref)
+    e = attn_errors(to_f64(r.o), o_ref)
     lerr = float(np.abs(r.lse.cpu().numpy() - lse_ref).max())
-    _say("  %s: max %.3e mean %.3e lse %.3e" % (name, mx, mean, lerr))
-    assert mx <= MAX_ERR and mean <= MEAN_ERR and lerr <= LSE_ERR
+    _say("  %s: %r lse %.3e" % (name, e, lerr))
+    assert e.ok() and lerr <= LSE_ERR, (e, lerr)
     if cfg.append:
         (start, tl, _), s = inp.segments[0], cfg.segments[0]
         n = s.n_frames * cfg.tokens_per_frame
@@ -302,8 +305,8 @@ def test_attention_identical_int8_inputs_mid():
     ref, _ = oracle.joint_attn(oracle.bf16_bits_to_f64(inp.q), oracle.bf16_bits_to_f64(inp.k),
                                oracle.bf16_bits_to_f64(inp.v),
                                [oracle.Segment(*s) for s in inp.segments], hk, hv, cfg.sm_scale)
-    mx, mean = attn_errors(to_f64(o), ref)
-    assert mx <= MAX_ERR and mean <= MEAN_ERR, (mx, mean)
+    e = attn_errors(to_f64(o), ref)
+    assert e.ok(), e
 
 
 def test_attention_deterministic_and_strided():
@@ -349,8 +352,8 @@ def test_edge_shapes():
         o = sc.segcausal_joint_attn(_bf(qb), _bf(kb), _bf(vb), [seg], 1.0)
         ref, _ = oracle.joint_attn(*(oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb)),
                                    [oracle.Segment(*seg)], sm_scale=1.0)
-        mx, mean = attn_errors(to_f64(o), ref)
-        assert mx <= MAX_ERR and mean <= MEAN_ERR, (n_cur, seg, mx, mean)
+        e = attn_errors(to_f64(o), ref)
+        assert e.ok(), (n_cur, seg, e)
     # empty call writes nothing
     z = torch.zeros((0, 2, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
     sc.segcausal_joint_attn(z, z, z, [(0, 0, 0)], 1.0)
@@ -423,8 +426,8 @@ def test_rows_without_visible_keys_in_early_tiles():
                                [oracle.Segment(*s) for s in segs], sm_scale=0.088)
     got = to_f64(o)
     assert np.isfinite(got).all()
-    mx, mean = attn_errors(got, ref)
-    assert mx <= MAX_ERR and mean <= MEAN_ERR, (mx, mean)
+    e = attn_errors(got, ref)
+    assert e.ok(), e
 
 
 # ----------------------------------------------------- c4 at full size ----
@@ -434,7 +437,7 @@ def test_c4_append_and_rope_bit_exact():
     cfg = workloads.CONFIGS["c4"]
     _say("c4 append")
     inp = workloads.make_inputs(cfg)
-    r = gpu_chain(inp, with_lse=False)
+    r = gpu_chain(inp, with_lse=True)
     s = cfg.segments[0]
     g, h = cfg.tokens_per_frame, cfg.n_heads
     # current segment: RoPE bit-exact on sampled frames, append codes bit-exact
@@ -451,12 +454,15 @@ def test_c4_append_and_rope_bit_exact():
         assert np.array_equal(r.cache.k_scale[slot].cpu().numpy(), ks)
         assert np.array_equal(r.cache.v[slot].cpu().numpy(), vc)
         assert np.array_equal(r.cache.v_scale[slot].cpu().numpy(), vs)
-    # history frames: sampled frames bit-exact
+    # history frames: K and V codes and scales of sampled frames bit-exact
     for f in rng.choice(288, size=6, replace=False):
         kf = oracle.rope3d_bf16(inp.hist_k[f * g:(f + 1) * g], inp.hist_pos[f * g:(f + 1) * g])
         kc, ks = oracle.quantise_int8(kf.transpose(1, 0, 2))
+        vc, vs = oracle.quantise_int8(oracle.bf16_bits_to_f64(inp.hist_v[f * g:(f + 1) * g]).transpose(1, 0, 2))
         assert np.array_equal(r.cache.k[f].cpu().numpy(), kc)
         assert np.array_equal(r.cache.k_scale[f].cpu().numpy(), ks)
+        assert np.array_equal(r.cache.v[f].cpu().numpy(), vc)
+        assert np.array_equal(r.cache.v_scale[f].cpu().numpy(), vs)
     # the BF16-window form of the same attention is bit-identical
     import torch
     win = _dequant_window(r.cache, r.slots)
@@ -468,11 +474,12 @@ def test_c4_append_and_rope_bit_exact():
     # attention on sampled rows, reading the cache exactly as the oracle builds it
     rows = np.concatenate([np.arange(0, 256, 4), 256 + rng.choice(cfg.n_video, 192, replace=False)])
     _say("c4 oracle rows", len(rows))
-    o_ref = _c4_rows_oracle(inp, rows)
+    o_ref, lse_ref = _c4_rows_oracle(inp, rows)
     got = to_f64(r.o[torch.from_numpy(rows).cuda()])
-    mx, mean = attn_errors(got, o_ref)
-    _say("  c4 sampled: max %.3e mean %.3e" % (mx, mean))
-    assert mx <= MAX_ERR and mean <= MEAN_ERR
+    e = attn_errors(got, o_ref)
+    lerr = float(np.abs(r.lse.cpu().numpy()[:, rows] - lse_ref).max())
+    _say("  c4 sampled: %r lse %.3e" % (e, lerr))
+    assert e.ok() and lerr <= LSE_ERR, (e, lerr)
 
 
 def _c4_rows_oracle(inp, rows):
@@ -492,5 +499,4 @@ def _c4_rows_oracle(inp, rows):
         hk[sl] = oracle.dequantise_int8(kc, ks)
         hv[sl] = oracle.dequantise_int8(vc, vs)
     segs = [oracle.Segment(*s) for s in inp.segments]
-    o, _ = oracle.joint_attn_rows(q, k, v, segs, rows, hk, hv, cfg.sm_scale)
-    return o
+    return oracle.joint_attn_rows(q, k, v, segs, rows, hk, hv, cfg.sm_scale)
