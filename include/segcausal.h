@@ -397,12 +397,30 @@ typedef struct segc_attn_bwd_args {
  */
 int segcausal_joint_attn_bwd(const segc_attn_bwd_args* args, void* stream);
 
+/*
+ * segcausal_joint_attn_bwd_noalloc -- segcausal_joint_attn_bwd for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). It takes the same
+ * arguments and computes the same gradients with the same kernels, but
+ * args->delta is ignored (it may be NULL): delta lives in a device array of
+ * 2^23 floats (32 MiB) inside the library, which each GPU the library runs on
+ * holds until the process ends. The call allocates nothing, does not
+ * synchronise, and on the first call on a device looks up that device's
+ * address of the array (the device must be current). Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on other streams or
+ * from other host threads) race and must be ordered by the caller.
+ * Errors: those of segcausal_joint_attn_bwd (delta excepted), and EINVAL when
+ *   n x n_heads exceeds 2^23; EHIP if the device or the array's address cannot
+ *   be queried.
+ */
+int segcausal_joint_attn_bwd_noalloc(const segc_attn_bwd_args* args, void* stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 7)
+#define SEGC_ABI_VERSION ((1 << 16) | 8)
 
 #ifdef __cplusplus
 }

@@ -81,15 +81,17 @@ _lib.kv_archive_fetch.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINT
 _lib.kv_archive_store.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
 _lib.segcausal_joint_attn_bwd.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
+_lib.segcausal_joint_attn_bwd_noalloc.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
 _lib.segcausal_last_error.restype = ctypes.c_char_p
 _lib.segcausal_abi_version.restype = ctypes.c_int
 for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
-           "w8a16_linear", "camera_cross_attn"):
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "segcausal_joint_attn_bwd_noalloc",
+           "kv_archive_fetch", "kv_archive_store", "w8a16_linear", "camera_cross_attn"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "kv_archive_fetch", "kv_archive_store",
+           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "segcausal_joint_attn_bwd_noalloc",
+           "kv_archive_fetch", "kv_archive_store",
            "w8a16_linear", "camera_cross_attn", "segcausal_last_error", "segcausal_abi_version")
 
 
@@ -383,14 +385,31 @@ def segcausal_joint_attn_bwd(q, k, v, o, dout, lse, segments, sm_scale, dq=None,
     dq, dk, dv       : optional bf16 [n, H, 128] outputs; delta: optional fp32
                        [H, n] workspace (receives rowsum(dout * o))
     """
+    return _attn_bwd(_lib.segcausal_joint_attn_bwd, q, k, v, o, dout, lse, segments, sm_scale,
+                     dq, dk, dv, delta, stream, True)
+
+
+def segcausal_joint_attn_bwd_noalloc(q, k, v, o, dout, lse, segments, sm_scale, dq=None, dk=None,
+                                     dv=None, stream=None):
+    """segcausal_joint_attn_bwd through the entry point that allocates nothing:
+    delta lives in the library's device scratch (n x H <= 2^23); calls that
+    overlap on one GPU race. Pass dq, dk, dv to keep this call free of torch
+    allocations too."""
+    return _attn_bwd(_lib.segcausal_joint_attn_bwd_noalloc, q, k, v, o, dout, lse, segments, sm_scale,
+                     dq, dk, dv, None, stream, False)
+
+
+def _attn_bwd(fn, q, k, v, o, dout, lse, segments, sm_scale, dq, dk, dv, delta, stream, workspace):
     n, nh = q.shape[0], q.shape[1]
     outs = []
     for t in (dq, dk, dv):
         outs.append(torch.empty_like(q, memory_format=torch.contiguous_format) if t is None else t)
     dq, dk, dv = outs
-    if delta is None:
+    if workspace and delta is None:
         delta = torch.empty((nh, n), dtype=torch.float32, device=q.device)
     for name, t in (("lse", lse), ("delta", delta)):
+        if t is None:
+            continue
         if t.dtype != torch.float32 or tuple(t.shape) != (nh, n) or not t.is_contiguous():
             raise ValueError("%s must be contiguous fp32 [H, n]" % name)
     rows = [_rows(t, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"),
@@ -402,9 +421,9 @@ def segcausal_joint_attn_bwd(q, k, v, o, dout, lse, segments, sm_scale, dq=None,
     strides = [x for r in rows for x in r[1:]]
     seg_start, tl, tv = _segment_tables(segments, n)
     args = SegcAttnBwdArgs(*([r[0] for r in rows] + strides +
-                             [lse.data_ptr(), delta.data_ptr(), n, nh, HEAD_DIM, len(segments), 0,
-                              seg_start, tl, tv, float(sm_scale)]))
-    _check(_lib.segcausal_joint_attn_bwd(ctypes.byref(args), _stream(stream)))
+                             [lse.data_ptr(), delta.data_ptr() if delta is not None else None, n, nh,
+                              HEAD_DIM, len(segments), 0, seg_start, tl, tv, float(sm_scale)]))
+    _check(fn(ctypes.byref(args), _stream(stream)))
     return dq, dk, dv
 
 

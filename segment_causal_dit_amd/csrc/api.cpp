@@ -169,6 +169,8 @@ int move_frames(const segc_cache* src, const int32_t* src_idx, const segc_cache*
 
 }  // namespace
 
+int segc::report(int code, const char* msg) { return fail(code, "%s", msg); }
+
 extern "C" {
 
 const char* segcausal_last_error(void) { return g_err; }
@@ -486,6 +488,14 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
 
 int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
   if (!a) return fail(SEGC_EINVAL, "args is NULL");
+  return segc::attn_bwd_checked(a, a->delta, stream);
+}
+
+}  // extern "C"
+
+// Checks and launches of the packed-form backward with the delta workspace
+// `delta` (the caller's, or the allocation-free entry point's device scratch).
+int segc::attn_bwd_checked(const segc_attn_bwd_args* a, float* delta, void* stream) {
   if (a->head_dim != SEGC_HEAD_DIM) return fail(SEGC_EUNSUPPORTED, "head_dim %d != 128", a->head_dim);
   if (a->n_seg < 1 || a->n_seg > SEGC_MAX_SEG)
     return fail(SEGC_EUNSUPPORTED, "n_seg %d outside [1, %d]", a->n_seg, SEGC_MAX_SEG);
@@ -511,13 +521,13 @@ int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
     if (!ptr[i]) return fail(SEGC_EINVAL, "NULL q/k/v/o/dout/dq/dk/dv");
     if (!aligned16(ptr[i])) return fail(SEGC_EINVAL, "q/k/v/o/dout/dq/dk/dv must be 16-byte aligned");
   }
-  if (!a->lse || !a->delta) return fail(SEGC_EINVAL, "NULL lse/delta");
-  if (((uintptr_t)a->lse & 3u) || ((uintptr_t)a->delta & 3u))
+  if (!a->lse || !delta) return fail(SEGC_EINVAL, "NULL lse/delta");
+  if (((uintptr_t)a->lse & 3u) || ((uintptr_t)delta & 3u))
     return fail(SEGC_EINVAL, "lse/delta must be 4-byte aligned");
   // outputs are written while inputs are still read: an output that starts
   // where another argument starts is an in-place call, which this computation
   // cannot do (interleaved views, e.g. one [n][3][H][128] buffer, are fine)
-  const void* all[10] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse, a->delta};
+  const void* all[10] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse, delta};
   const char* names[10] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv", "lse", "delta"};
   const int outs[4] = {5, 6, 7, 9};
   for (int oi = 0; oi < 4; ++oi)
@@ -537,7 +547,7 @@ int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
   p.dk = (uint16_t*)a->dk;
   p.dv = (uint16_t*)a->dv;
   p.lse = a->lse;
-  p.delta = a->delta;
+  p.delta = delta;
   p.q_st = a->q_stride_tok;
   p.q_sh = a->q_stride_head;
   p.k_st = a->k_stride_tok;
@@ -569,5 +579,3 @@ int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
   return hip_status(segc::launch_attn_bwd(p, (hipStream_t)stream), "segcausal_joint_attn_bwd launch");
 }
-
-}  // extern "C"

@@ -114,6 +114,11 @@ struct AttnBwdParams {
 };
 hipError_t launch_attn_bwd(const AttnBwdParams& p, hipStream_t s);
 
+// Host side (api.cpp): the backward's argument checks and launches with the
+// delta workspace given separately, and the error reporting of the ABI.
+int attn_bwd_checked(const segc_attn_bwd_args* a, float* delta, void* stream);
+int report(int code, const char* msg);
+
 // Linear with INT8 weights: y[M][N] = bf16(scale[n] * x[M][K] . code[n][K] + bias[n]).
 struct W8GemmParams {
   const uint16_t* x;         // bf16 [M][ldx]

@@ -533,3 +533,21 @@ def test_launch_without_a_device_reports_hip_error():
         assert call() == sc.SEGC_EHIP
         msg = lib.segcausal_last_error().decode()
         assert "launch" in msg and len(msg) > len("launch: ")
+
+
+def test_noalloc_backward_refuses_beyond_its_scratch_on_the_host():
+    # n x n_heads above the 2^23 delta entries of the device scratch: refused
+    # before any device access (stand-in pointers are never touched)
+    starts = (ctypes.c_int32 * 2)(0, (1 << 22) + 1)
+    ptrs = [FAKE2 + i * 0x1000000 for i in range(len(_BWD_PTRS))]
+    a = sc.SegcAttnBwdArgs(*(ptrs + [256, 128] * 8 +
+                             [FAKE2 + 8 * 0x1000000, None, (1 << 22) + 1, 2, 128, 1, 0,
+                              starts, (ctypes.c_int32 * 1)(0), (ctypes.c_int32 * 1)(0), 0.088]))
+    assert lib.segcausal_joint_attn_bwd_noalloc(ctypes.byref(a), None) == sc.SEGC_EINVAL
+    assert "2^23" in lib.segcausal_last_error().decode()
+    assert lib.segcausal_joint_attn_bwd_noalloc(None, None) == sc.SEGC_EINVAL
+    # n == 0 is a no-op, and n < 0 is refused, both without a device
+    a.n, a.seg_start = 0, (ctypes.c_int32 * 2)(0, 0)
+    assert lib.segcausal_joint_attn_bwd_noalloc(ctypes.byref(a), None) == sc.SEGC_OK
+    a.n = -1
+    assert lib.segcausal_joint_attn_bwd_noalloc(ctypes.byref(a), None) == sc.SEGC_EINVAL
