@@ -75,6 +75,91 @@ def measured_traffic(cfg, path):
     return s.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name (for the CPU baseline's context)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def config_rates(names, reps=20):
+    """Attention at the shorter configurations, timed like the main line: the
+    history appended through the library (INT8 windows expanded to bf16 once,
+    as in the step), then `reps` attention launches timed with HIP events on
+    the launch stream. Returns {name: {...}} with each one's own roofline
+    fraction."""
+    import torch
+    import segment_causal_dit_amd as sc
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = {}
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for name in names:
+        cfg = workloads.CONFIGS[name]
+        inp = workloads.make_inputs(cfg)
+        q, k, v = bf(inp.q), bf(inp.k), bf(inp.v)
+        tl = cfg.segments[0].text_len
+        pos = torch.from_numpy(inp.pos).to(dev)
+        sc.rope3d_apply(q[tl:], pos)
+        sc.rope3d_apply(k[tl:], pos)
+        cache = hist = None
+        deq_ms = None
+        if len(cfg.hist_t):
+            cache = sc.KVCache(cfg.n_slots, cfg.n_heads, cfg.tokens_per_frame, cfg.cache_dtype, dev)
+            hk = bf(inp.hist_k)
+            sc.rope3d_apply(hk, torch.from_numpy(inp.hist_pos).to(dev))
+            sc.kv_cache_append(cache, 0, hk, bf(inp.hist_v))
+            cache.slot_t[:] = inp.slot_t
+            hist = torch.from_numpy(sc.window_select(cache.slot_t, cfg.window)).to(dev)
+            if cfg.cache_dtype == "int8":
+                win = sc.KVCache(len(hist), cfg.n_heads, cfg.tokens_per_frame, "bf16", dev)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                sc.kv_window_dequant(cache, hist, win)
+                a.record(stream)
+                sc.kv_window_dequant(cache, hist, win)
+                b.record(stream)
+                torch.cuda.synchronize()
+                deq_ms = a.elapsed_time(b)
+                cache, hist = win, torch.arange(len(hist), dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+
+        def call():
+            sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist, out=o)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        med = ms[len(ms) // 2]
+        tflops = cfg.flops() / (med * 1e-3) / 1e12
+        out[name] = {"attn_ms_median": round(med, 4), "attn_ms_min": round(ms[0], 4),
+                     "tflops": round(tflops, 2), "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "window_dequant_ms": round(deq_ms, 4) if deq_ms is not None else None,
+                     "n_cur": cfg.n_cur, "n_hist_keys": cfg.n_hist_rows, "cache": cfg.cache_dtype
+                     if len(cfg.hist_t) else None}
+        log("%s: attention %.4f ms (median of %d), %.1f TFLOP/s, %.1f%% of bf16 peak"
+            % (name, med, reps, tflops, 100 * tflops / PEAK_BF16_TFLOPS))
+        del q, k, v, o, cache, hist
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, inp, n_rows=512):
     """The fp64 oracle's attention on a bounded sample of the workload: all
     heads of n_rows random query rows against every key. History codes are
@@ -95,7 +180,7 @@ def cpu_baseline(cfg, inp, n_rows=512):
     dt = time.perf_counter() - t0
     flops = 4 * HEAD_DIM * h * n_rows * (cfg.n_hist_rows + cfg.n_cur)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "attention of %d random query rows x %d heads over all %d keys "
                       "(numpy float64, %d threads, %.1f s)"
                       % (n_rows, h, cfg.n_hist_rows + cfg.n_cur, cores, dt)}
@@ -142,9 +227,14 @@ def counters_workload(cfg_name):
     log("counters workload done")
 
 
-def summarize_counters(cfg_name, fetch_dir, write_dir, out_path):
+DRAM_READ, DRAM_WRITE = "TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"
+
+
+def summarize_counters(cfg_name, fetch_dir, write_dir, out_path, dram_dir=None):
     """Turn two rocprofv3 --pmc CSV outputs (FETCH_SIZE, WRITE_SIZE) into HBM
-    bytes per attention launch, scaled by the calibration copy."""
+    bytes per attention launch, scaled by the calibration copy; with a third
+    (the L2's 32-byte read and write requests to the memory controller), the
+    same from those counters beside it."""
     import csv
     import glob
 
@@ -165,6 +255,17 @@ def summarize_counters(cfg_name, fetch_dir, write_dir, out_path):
     w_scale = COPY_BYTES / 1024.0 / w_copy
     fetch = float(np.mean(f_attn)) * 1024.0 * f_scale
     write = float(np.mean(w_attn)) * 1024.0 * w_scale
+    dram = None
+    if dram_dir:
+        r_copy, r_attn = read(dram_dir, DRAM_READ)
+        x_copy, x_attn = read(dram_dir, DRAM_WRITE)
+        dram = {"read_bytes_per_launch": float(np.mean(r_attn)) * 32.0,
+                "write_bytes_per_launch": float(np.mean(x_attn)) * 32.0,
+                "calibration": {"copy_bytes": COPY_BYTES, "read_bytes_counted": r_copy * 32.0,
+                                "write_bytes_counted": x_copy * 32.0,
+                                "read_ratio": r_copy * 32.0 / COPY_BYTES,
+                                "write_ratio": x_copy * 32.0 / COPY_BYTES},
+                "counters": [DRAM_READ, DRAM_WRITE]}
     summary = {
         "workload": cfg_name, "kernel": ATTN_KERNEL, "attn_source_sha": attn_source_hash(),
         "history_path": history_path(workloads.CONFIGS[cfg_name]),
@@ -172,12 +273,16 @@ def summarize_counters(cfg_name, fetch_dir, write_dir, out_path):
         "hbm_bytes_per_launch": fetch + write,
         "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib_read": f_copy,
                         "write_kib_read": w_copy, "fetch_scale": f_scale, "write_scale": w_scale},
+        "dram_requests": dram,
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- "
             "python3 bench.py --config %s --counters-workload" % cfg_name,
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- "
             "python3 bench.py --config %s --counters-workload" % cfg_name,
-            "python3 bench.py --config %s --summarize-counters <fetch_dir> <write_dir>" % cfg_name],
+            "rocprofv3 --pmc %s %s --output-format csv -d <dram_dir> -- "
+            "python3 bench.py --config %s --counters-workload" % (DRAM_READ, DRAM_WRITE, cfg_name),
+            "python3 bench.py --config %s --summarize-counters <fetch_dir> <write_dir> [<dram_dir>]"
+            % cfg_name],
     }
     with open(out_path, "w") as f:
         json.dump(summary, f, indent=1)
@@ -203,7 +308,7 @@ def cpu_baseline_train(cfg, n_rows=16384):
     dt = time.perf_counter() - t0
     flops = 14 * HEAD_DIM * pairs
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": os.cpu_count() or 1,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "forward+backward of the first %d rows of one segment, 1 head "
                       "(numpy float64, %.1f s)" % (n_rows, dt)}
 
@@ -448,7 +553,7 @@ def archive_bench(args):
             reps += 1
         dt = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(reps * fetch_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-                                "kind": "oracle",
+                                "cpu_model": cpu_model(), "kind": "oracle",
                                 "sample": "the oracle's indexed copy of the same %d frames in host memory, "
                                           "%d repetitions in %.1f s" % (window, reps, dt)}
         del dst
@@ -549,7 +654,7 @@ def linear_bench(args):
             flops += 2 * m * n * k
             del xs
         line["cpu_baseline"] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-                                "cores": os.cpu_count() or 1, "kind": "oracle",
+                                "cores": os.cpu_count() or 1, "cpu_model": cpu_model(), "kind": "oracle",
                                 "sample": "all four linears at full size (numpy float64 matmul, %.1f s)" % dt}
     else:
         line["cpu_baseline"] = None
@@ -629,7 +734,7 @@ def camera_bench(args):
         oracle.camera_cross_attn(qs, ks, vs, tpc, 4, 1.0 / math.sqrt(HEAD_DIM))
         dt = time.perf_counter() - t
         line["cpu_baseline"] = {"value": round(rows * h * HEAD_DIM * 2 * 2 / dt / 1e9, 3), "unit": "GB/s",
-                                "cores": 1, "kind": "oracle",
+                                "cores": 1, "cpu_model": cpu_model(), "kind": "oracle",
                                 "sample": "the oracle's softmax path on all 72 latent frames (63,360 rows x 16 "
                                           "heads, 4 camera tokens each; numpy float64, %.1f s)" % dt}
     else:
@@ -644,12 +749,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c4", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the c1-c3 attention rates reported beside the c4 line")
     ap.add_argument("--int8-attn", choices=("window", "cache"), default="window",
                     help="INT8 history: expand the window to bf16 once per layer-step (window) "
                          "or dequantise inside every attention workgroup (cache)")
     ap.add_argument("--counters-workload", action="store_true",
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR [DRAM_DIR]: rocprofv3 --pmc outputs to summarise")
     ap.add_argument("--camera", action="store_true",
                     help="the per-latent-frame camera cross-attention instead")
     ap.add_argument("--linear", action="store_true",
@@ -662,8 +770,12 @@ def main():
                          "attention over 13 packed segments (346,528 rows)")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(args.config, args.summarize_counters[0], args.summarize_counters[1],
-                           os.path.join(ROOT, "profiles", "attn_%s_counters.json" % args.config))
+        d = args.summarize_counters
+        if len(d) not in (2, 3):
+            ap.error("--summarize-counters takes FETCH_DIR WRITE_DIR [DRAM_DIR]")
+        summarize_counters(args.config, d[0], d[1],
+                           os.path.join(ROOT, "profiles", "attn_%s_counters.json" % args.config),
+                           d[2] if len(d) == 3 else None)
         return
     if args.counters_workload:
         counters_workload(args.config)
@@ -842,10 +954,13 @@ def main():
     if expand:
         line["int8_cache_attention"] = {"ms": round(fused_ms, 4), "tflops": round(fused_tflops, 3),
                                         "frac": round(fused_tflops / PEAK_BF16_TFLOPS, 4)}
+    del q_pre, k_pre, q, k, v, out, cache, win
+    torch.cuda.empty_cache()
+    if args.config == "c4" and not args.no_other_configs:
+        # the shorter configurations' attention, each against its own roofline
+        line["other_configs"] = config_rates(["c1", "c2", "c3"])
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
-        del q_pre, k_pre, q, k, v, out, cache, win
-        torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     else:
         line["cpu_baseline"] = None
