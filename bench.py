@@ -228,6 +228,8 @@ def counters_workload(cfg_name):
 
 
 DRAM_READ, DRAM_WRITE = "TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"
+# counter passes profile only the attention and the calibration copy
+KERNEL_FILTER = "--kernel-include-regex 'attn_kernel|elementwise|copy'"
 
 
 def summarize_counters(cfg_name, fetch_dir, write_dir, out_path, dram_dir=None):
@@ -275,12 +277,12 @@ def summarize_counters(cfg_name, fetch_dir, write_dir, out_path, dram_dir=None):
                         "write_kib_read": w_copy, "fetch_scale": f_scale, "write_scale": w_scale},
         "dram_requests": dram,
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -- "
-            "python3 bench.py --config %s --counters-workload" % cfg_name,
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <write_dir> -- "
-            "python3 bench.py --config %s --counters-workload" % cfg_name,
-            "rocprofv3 --pmc %s %s --output-format csv -d <dram_dir> -- "
-            "python3 bench.py --config %s --counters-workload" % (DRAM_READ, DRAM_WRITE, cfg_name),
+            "rocprofv3 --pmc FETCH_SIZE %s --output-format csv -d <fetch_dir> -- "
+            "python3 bench.py --config %s --counters-workload" % (KERNEL_FILTER, cfg_name),
+            "rocprofv3 --pmc WRITE_SIZE %s --output-format csv -d <write_dir> -- "
+            "python3 bench.py --config %s --counters-workload" % (KERNEL_FILTER, cfg_name),
+            "rocprofv3 --pmc %s %s %s --output-format csv -d <dram_dir> -- "
+            "python3 bench.py --config %s --counters-workload" % (DRAM_READ, DRAM_WRITE, KERNEL_FILTER, cfg_name),
             "python3 bench.py --config %s --summarize-counters <fetch_dir> <write_dir> [<dram_dir>]"
             % cfg_name],
     }

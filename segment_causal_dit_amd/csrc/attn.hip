@@ -19,16 +19,21 @@
 // workgroup per CU, two waves per SIMD):
 //  * each wave owns 32 query rows; Q stays in registers as MFMA B operands;
 //  * key tiles of 64 rows are staged through LDS by direct global->LDS
-//    loads (no staging registers), two tiles ahead in three tile buffers:
-//    the loads issued while tile t is computed belong to tile t+2 and have a
-//    whole tile's time to land before the waves wait for them; waves 0-3
-//    stage, so each SIMD hosts one staging wave and one compute-only wave;
-//    the loads are issued
-//    from inline assembly and awaited explicitly once per tile, because the
-//    compiler, unable to tell the two LDS buffers apart, would otherwise
-//    drain them before every operand read of the other buffer; all slot
-//    lookups precede the loads of a tile (a wait for a lookup would drain
-//    them too);
+//    loads (no staging registers); waves 0-3 stage, so each SIMD hosts one
+//    staging wave and one compute-only wave. Two schedules:
+//    - bf16 keys (a BF16 cache, or no history): two tiles per barrier,
+//      double buffered -- while tiles 2u and 2u+1 are computed from one
+//      128-key buffer, the loads of tiles 2u+2 and 2u+3 land in the other
+//      (one barrier, one wait and one round of staging bookkeeping per 128
+//      keys);
+//    - an INT8 history: one tile per barrier, three tile buffers, loads two
+//      tiles ahead, and two staging areas for the codes and scales (the
+//      128-key buffers and the INT8 staging would not fit the 160 KB LDS);
+//    the loads are issued from inline assembly and awaited explicitly, once
+//    per barrier, because the compiler, unable to tell the LDS buffers
+//    apart, would otherwise drain them before every operand read of another
+//    buffer; all slot lookups precede the loads of a tile (a wait for a
+//    lookup would drain them too);
 //  * tiles are row-major with XOR-swizzled 16-byte chunks, chosen for the
 //    gfx950 LDS (16 lanes of a 16-byte read per cycle over 64 banks) so that
 //    every operand read is conflict-free and every load instruction moves 4
@@ -50,9 +55,14 @@
 //  * INT8 history rows (codes and scales) are direct-loaded into one of two
 //    staging areas and dequantised to bf16(code * scale) into the tile by the
 //    wave that loaded them, so the MFMA path is the same for both cache types;
-//  * online softmax in base 2 with the rescale of O deferred until the running
-//    max grows by more than 2^8 (exact: the final division uses the same
-//    reference max);
+//  * online softmax in base 2 against a per-row reference max that moves
+//    only when needed: a tile's exponentials are taken against the current
+//    reference and summed (the row sum needs them anyway); only when that
+//    per-lane sum exceeds 2^12 (so some exponential might, or has
+//    overflowed) or the row has seen no visible key yet does the wave form
+//    the logits again, take the true tile max, rescale O and l and redo the
+//    exponentials. No per-tile max reduction remains on the common path,
+//    and the result is exact: the final division uses the same reference;
 //  * masks are per tile: only tiles at a ragged end, or with text rows, or
 //    with video of a segment later than the workgroup's first query evaluate
 //    a per-element predicate from a 64-entry key table in LDS; keys of later
@@ -82,7 +92,9 @@ constexpr int RAW0 = NBUF * BUF_BYTES;           // two INT8 staging areas: code
 constexpr int RAW_KC = 0, RAW_VC = BN * D, RAW_S = 2 * BN * D;
 constexpr int RAW_BYTES = 2 * BN * D + NSTAGE * 256;   // codes + one 64-float scale block per wave
 constexpr int LDS_BYTES = RAW0 + 2 * RAW_BYTES;
-constexpr float kTau = 8.0f;           // deferred-rescale threshold (log2 units)
+// pair schedule (bf16 keys only): two 64-key tiles per barrier, two 128-key buffers
+constexpr int PAIR_BYTES = 2 * BUF_BYTES;
+constexpr int LDS_PAIR_BYTES = 2 * PAIR_BYTES;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -231,10 +243,13 @@ __device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ (5 * (r & 3))
 // Issue the loads of staging wave w's group of tile tl: bf16 rows go
 // straight into the K/V tiles of `buf`; INT8 history rows go into `raw`
 // (codes, plus the group's K and V scales) for stage_finish to convert.
+// kInt8 = false compiles the INT8 branch out (the pair schedule never sees
+// INT8 rows).
+template <bool kInt8 = true>
 __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, int lane, int head,
                                   char* buf, char* raw) {
   const Group g = group_at(p, tl, w, head);
-  if (!tl.hist || !p.hist_int8) {
+  if (!kInt8 || !tl.hist || !p.hist_int8) {
     if (g.lim >= RW - 1 && !g.generic) {
       // a whole group (no clamping) of consecutive rows of one frame or of the
       // current rows: a uniform base per tensor, and per-lane offsets that only
@@ -385,37 +400,64 @@ struct RowState {
   float m, l;
 };
 
-// Softmax of one tile (in place: s becomes p) and O rescale when needed.
-__device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info, int qseg, int hh,
-                                    float c, RowState& rs, f32x16 (&o)[4]) {
-  if (masked) {
+// Exponentials of one tile, in place (s becomes p), against the row's
+// reference max m, and their per-lane sum ls. The reference moves only when
+// the tile's exponentials would outgrow kPLimit (their per-lane sum says so:
+// every term is at most the sum; an infinite or NaN sum fails the test too)
+// or while the row has seen no visible key; then the logits are formed again
+// from the K tile (still in LDS), the true tile max is taken, O and l are
+// rescaled and the exponentials recomputed. Any reference no larger than the
+// row max gives the same softmax: the final division uses the same reference.
+constexpr float kPLimit = 0x1p12f;
+
+__device__ inline float exp_sum(f32x16 (&s)[2], float c, float mc) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int j = 0; j < 32; ++j) s[j >> 4][j & 15] = __builtin_amdgcn_exp2f(fmaf(s[j >> 4][j & 15], c, -mc));
+  float t[16];
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const i32x4 inf4 = *(const i32x4*)(info + 32 * kb + 8 * jq + 4 * hh);
+  for (int j = 0; j < 16; ++j) t[j] = s[0][j] + s[1][j];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int lo = inf4[jj] & 0xFFFF, hi = (inf4[jj] >> 16) & 0xFFFF;
-          if (qseg < lo || qseg > hi) s[kb][4 * jq + jj] = -INFINITY;
-        }
+  for (int j = 0; j < 8; ++j) t[j] = t[j] + t[j + 8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = t[j] + t[j + 4];
+  return (t[0] + t[2]) + (t[1] + t[3]);
+}
+
+__device__ inline void mask_tile(f32x16 (&s)[2], const int* info, int qseg, int hh) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const i32x4 inf4 = *(const i32x4*)(info + 32 * kb + 8 * jq + 4 * hh);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int lo = inf4[jj] & 0xFFFF, hi = (inf4[jj] >> 16) & 0xFFFF;
+        if (qseg < lo || qseg > hi) s[kb][4 * jq + jj] = -INFINITY;
       }
-  }
-  // tile max as a tree of 3-input maxima (depth 4 rather than a 16-deep chain)
-  float m1[11];
-#pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
-    m1[i] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[e >> 4][e & 15]);
-  }
-  m1[10] = fmaxf(s[1][14], s[1][15]);
-  const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]), m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
-  const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]), m2d = fmaxf(m1[9], m1[10]);
-  float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
-  mx = xhalf_max(mx);
-  const float mnew = fmaxf(rs.m, mx);
-  const bool need = (mnew - rs.m) * c > kTau;          // false for -inf/-inf (NaN)
+    }
+}
+
+__device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info, int qseg, int hh,
+                                    float c, RowState& rs, f32x16 (&o)[4], float& ls,
+                                    const char* kbuf, const bf16x8 (&qf)[8], int lr) {
+  if (masked) mask_tile(s, info, qseg, hh);
+  ls = exp_sum(s, c, (rs.m == -INFINITY) ? 0.0f : rs.m * c);
+  const bool need = !(ls <= kPLimit) || rs.m == -INFINITY;
   if (__builtin_amdgcn_ballot_w64(need)) {
+    qk_tile(kbuf, qf, lr, hh, s);
+    if (masked) mask_tile(s, info, qseg, hh);
+    float m1[11];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
+      m1[i] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[e >> 4][e & 15]);
+    }
+    m1[10] = fmaxf(s[1][14], s[1][15]);
+    const float m2a = fmaxf(fmaxf(m1[0], m1[1]), m1[2]), m2b = fmaxf(fmaxf(m1[3], m1[4]), m1[5]);
+    const float m2c = fmaxf(fmaxf(m1[6], m1[7]), m1[8]), m2d = fmaxf(m1[9], m1[10]);
+    float mx = fmaxf(fmaxf(m2a, m2b), fmaxf(m2c, m2d));
+    mx = xhalf_max(mx);
+    const float mnew = fmaxf(rs.m, mx);
     // a row that has seen no visible key yet keeps m = -inf: its factor is 1
     // (exp2 of -inf - -inf would be NaN and poison O and l for good)
     const float alpha = (mnew == rs.m) ? 1.0f : __builtin_amdgcn_exp2f((rs.m - mnew) * c);
@@ -425,22 +467,18 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+    ls = exp_sum(s, c, (rs.m == -INFINITY) ? 0.0f : rs.m * c);
   }
-  const float mc = (rs.m == -INFINITY) ? 0.0f : rs.m * c;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][j], c, -mc));
 }
 
-// O^T += V^T P^T for one tile; the row sum l accumulates the fp32 P values.
+// O^T += V^T P^T for one tile (p from s, rounded to bf16 as the operand).
 // The V^T operand comes from the row-major V tile through the transposing
 // LDS read: inside each 16-lane group, lane j addresses 4 elements of row
 // base + j/4 at column d0 + 4 (j % 4); lane i then receives rows base..base+3
 // at column d0 + i, i.e. 4 keys of its own d. Two reads give the 8 keys the
 // P operand holds in this lane half (rows 16 ck + 4 hh + 0..3 and + 8..11).
 __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane, int hh,
-                               f32x16 (&o)[4], RowState& rs) {
+                               f32x16 (&o)[4]) {
   // lane i of 16-lane group g reads row 16 ck + 4 hh + i / 4 and the row 8
   // further down, column 32 db + 16 (g & 1) + 4 (i % 4): chunk 4 db + hb with
   // hb = 2 (g & 1) + (i % 4) / 2, byte 8 (i & 1).
@@ -448,16 +486,16 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
   const int hb = ((gi & 3) >> 1) | (((lane >> 4) & 1) << 1);
   const int r0 = 4 * hh + (gi >> 2);
   const int sub = 8 * (gi & 1);
-  float ls = 0.0f;
 #pragma unroll
   for (int ck = 0; ck < 4; ++ck) {
-    u32x4 u;
+    // the four packed pairs go into a plain array first and into the vector
+    // in one piece (writing vector elements one by one inside unrolled loops
+    // has been seen to lose some of them in this compiler's output)
+    uint32_t wd[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = s[ck >> 1][8 * (ck & 1) + 2 * e], x1 = s[ck >> 1][8 * (ck & 1) + 2 * e + 1];
-      u[e] = pack_bf16(x0, x1);
-      ls += x0 + x1;
-    }
+    for (int e = 0; e < 4; ++e)
+      wd[e] = pack_bf16(s[ck >> 1][8 * (ck & 1) + 2 * e], s[ck >> 1][8 * (ck & 1) + 2 * e + 1]);
+    const u32x4 u = {wd[0], wd[1], wd[2], wd[3]};
     const bf16x8 pb = as_bf16x8(u);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -477,10 +515,6 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  // use the sum here: otherwise its adds sink below the staging branch that
-  // follows and run, with no products left to hide them, before the barrier
-  asm volatile("" :: "v"(ls));
-  rs.l += ls;
 }
 
 // Finish staging wave w's group of tile tl: wait for its direct loads, turn
@@ -507,7 +541,7 @@ __device__ inline void stage_finish(const AttnParams& p, const Tile& tl, int w, 
   if (masked) store_info<kSeg>(p, tl, tid, (int*)(buf + IOFF), sg);
 }
 
-template <bool kSeg>
+template <bool kSeg, bool kPair>
 __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -561,50 +595,107 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   RowState rs = {-INFINITY, 0.0f};
   const float c = p.scale_log2;
 
-  // Lockstep schedule, one barrier per tile, loads two tiles ahead: during
-  // iteration t every wave computes tile t from LDS buffer t % 3 while the
-  // staging waves' direct loads for tile t+2 land in buffer (t+2) % 3 (bf16)
-  // or INT8 staging area t & 1; at the end of the iteration they wait for
-  // tile t+1's loads (issued one iteration earlier) and dequantise it.
   const bool stager = w < NSTAGE;
-  char* const raw0 = smem + RAW0;
-  char* const raw1 = smem + RAW0 + RAW_BYTES;
-  // every wave walks the mask state (scalar work); the next tile's decision
-  // is made after this tile's products are issued
-  bool mt = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
-  if (stager) {
-    const Tile t0 = tile_at(p, 0, cur_end);
-    stage_issue(p, t0, w, lane, head, smem, raw0);
-    stage_finish<kSeg>(p, t0, w, lane, tid, smem, raw0, 0, mt, mw.kseg.s);
-    if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, raw1);
-  }
-  __syncthreads();
-  int bc = 0;
-  for (int t = 0; t < n_tiles; ++t) {
-    char* const cur = smem + bc * BUF_BYTES;
-    char* const nx1 = smem + (bc == NBUF - 1 ? 0 : bc + 1) * BUF_BYTES;
-    char* const nx2 = smem + (bc == 0 ? NBUF - 1 : bc - 1) * BUF_BYTES;
-    const int* info = (const int*)(cur + IOFF);
-    // nothing is outstanding here (the barrier drained LDS; scalar loads are
-    // consumed where issued), but a scalar load hoisted before the loop would
-    // otherwise make the compiler wait for every LDS read ahead of the first
-    // product of each tile (scalar and LDS loads share a counter, and scalar
-    // loads complete out of order)
-    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
-    int issued = 0;
-    if (stager && t + 2 < n_tiles)
-      issued = stage_issue(p, tile_at(p, t + 2, cur_end), w, lane, head, nx2, (t & 1) ? raw1 : raw0);
-    f32x16 sc[2];
-    qk_tile(cur + KOFF, qf, lr, hh, sc);
-    softmax_tile(sc, mt, info, qseg, hh, c, rs, o);
-    pv_tile(cur + VOFF, sc, lane, hh, o, rs);
-    const bool mt_next = t + 1 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t + 1, cur_end), mw);
-    if (stager && t + 1 < n_tiles)
-      stage_finish<kSeg>(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued, mt_next,
-                   mw.kseg.s);
+  if constexpr (kPair) {
+    // Two tiles per barrier, double buffered: during iteration u every wave
+    // computes tiles 2u and 2u+1 from buffer u % 2 while the staging waves'
+    // direct loads for tiles 2u+2 and 2u+3 land in the other buffer; at the
+    // end of the iteration they wait for those loads (issued a whole
+    // iteration earlier) and write the key tables of tiles that need a mask.
+    // The mask walk visits the tiles in ascending order, once each.
+    auto half = [&](const char* buf, bool masked) {
+      const int* info = (const int*)(buf + IOFF);
+      f32x16 sc[2];
+      qk_tile(buf + KOFF, qf, lr, hh, sc);
+      float ls;
+      softmax_tile(sc, masked, info, qseg, hh, c, rs, o, ls, buf + KOFF, qf, lr);
+      rs.l += ls;
+      pv_tile(buf + VOFF, sc, lane, hh, o);
+    };
+    bool m0t = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
+    const int s0 = mw.kseg.s;
+    bool m1t = n_tiles > 1 && tile_masked<kSeg>(p, tile_at(p, 1, cur_end), mw);
+    const int s1 = mw.kseg.s;
+    if (stager) {
+      stage_issue<false>(p, tile_at(p, 0, cur_end), w, lane, head, smem, nullptr);
+      if (n_tiles > 1) stage_issue<false>(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, nullptr);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (m0t) store_info<kSeg>(p, tile_at(p, 0, cur_end), tid, (int*)(smem + IOFF), s0);
+      if (m1t) store_info<kSeg>(p, tile_at(p, 1, cur_end), tid, (int*)(smem + BUF_BYTES + IOFF), s1);
+    }
     __syncthreads();
-    mt = mt_next;
-    bc = (bc == NBUF - 1) ? 0 : bc + 1;
+    const int n_pairs = (n_tiles + 1) >> 1;
+    for (int u = 0; u < n_pairs; ++u) {
+      char* const cur = smem + (u & 1) * PAIR_BYTES;
+      char* const nxt = smem + ((u & 1) ^ 1) * PAIR_BYTES;
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
+      const int t0 = 2 * u;
+      if (stager && t0 + 2 < n_tiles) {
+        stage_issue<false>(p, tile_at(p, t0 + 2, cur_end), w, lane, head, nxt, nullptr);
+        if (t0 + 3 < n_tiles) stage_issue<false>(p, tile_at(p, t0 + 3, cur_end), w, lane, head, nxt + BUF_BYTES, nullptr);
+      }
+      half(cur, m0t);
+      if (t0 + 1 < n_tiles) half(cur + BUF_BYTES, m1t);
+      const bool n0 = t0 + 2 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t0 + 2, cur_end), mw);
+      const int sg0 = mw.kseg.s;
+      const bool n1 = t0 + 3 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t0 + 3, cur_end), mw);
+      const int sg1 = mw.kseg.s;
+      if (stager && t0 + 2 < n_tiles) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (n0) store_info<kSeg>(p, tile_at(p, t0 + 2, cur_end), tid, (int*)(nxt + IOFF), sg0);
+        if (n1) store_info<kSeg>(p, tile_at(p, t0 + 3, cur_end), tid, (int*)(nxt + BUF_BYTES + IOFF), sg1);
+      }
+      __syncthreads();
+      m0t = n0;
+      m1t = n1;
+    }
+  } else {
+    // One tile per barrier (an INT8 history), loads two tiles ahead: during
+    // iteration t every wave computes tile t from LDS buffer t % 3 while the
+    // staging waves' direct loads for tile t+2 land in buffer (t+2) % 3 (bf16)
+    // or INT8 staging area t & 1; at the end of the iteration they wait for
+    // tile t+1's loads (issued one iteration earlier) and dequantise it.
+    char* const raw0 = smem + RAW0;
+    char* const raw1 = smem + RAW0 + RAW_BYTES;
+    // every wave walks the mask state (scalar work); the next tile's decision
+    // is made after this tile's products are issued
+    bool mt = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
+    if (stager) {
+      const Tile t0 = tile_at(p, 0, cur_end);
+      stage_issue(p, t0, w, lane, head, smem, raw0);
+      stage_finish<kSeg>(p, t0, w, lane, tid, smem, raw0, 0, mt, mw.kseg.s);
+      if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, raw1);
+    }
+    __syncthreads();
+    int bc = 0;
+    for (int t = 0; t < n_tiles; ++t) {
+      char* const cur = smem + bc * BUF_BYTES;
+      char* const nx1 = smem + (bc == NBUF - 1 ? 0 : bc + 1) * BUF_BYTES;
+      char* const nx2 = smem + (bc == 0 ? NBUF - 1 : bc - 1) * BUF_BYTES;
+      const int* info = (const int*)(cur + IOFF);
+      // nothing is outstanding here (the barrier drained LDS; scalar loads are
+      // consumed where issued), but a scalar load hoisted before the loop would
+      // otherwise make the compiler wait for every LDS read ahead of the first
+      // product of each tile (scalar and LDS loads share a counter, and scalar
+      // loads complete out of order)
+      __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
+      int issued = 0;
+      if (stager && t + 2 < n_tiles)
+        issued = stage_issue(p, tile_at(p, t + 2, cur_end), w, lane, head, nx2, (t & 1) ? raw1 : raw0);
+      f32x16 sc[2];
+      qk_tile(cur + KOFF, qf, lr, hh, sc);
+      float ls;
+      softmax_tile(sc, mt, info, qseg, hh, c, rs, o, ls, cur + KOFF, qf, lr);
+      rs.l += ls;
+      pv_tile(cur + VOFF, sc, lane, hh, o);
+      const bool mt_next = t + 1 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t + 1, cur_end), mw);
+      if (stager && t + 1 < n_tiles)
+        stage_finish<kSeg>(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued, mt_next,
+                     mw.kseg.s);
+      __syncthreads();
+      mt = mt_next;
+      bc = (bc == NBUF - 1) ? 0 : bc + 1;
+    }
   }
 
   // epilogue: O = acc / l, bf16; lse = m * sm_scale + ln l
@@ -632,13 +723,20 @@ hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
   p.n_qtiles = (p.n_cur + BM - 1) / BM;
   const int64_t nwg = (int64_t)p.n_qtiles * p.n_heads;
   // more than 64 KB of dynamic LDS must be allowed explicitly (gfx950 has 160 KB per CU)
-  const void* fn = p.needs_mask ? (const void*)attn_kernel<true> : (const void*)attn_kernel<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  const bool pair = !(p.hist_tiles > 0 && p.hist_int8);
+  const void* fn = p.needs_mask ? (pair ? (const void*)attn_kernel<true, true> : (const void*)attn_kernel<true, false>)
+                                : (pair ? (const void*)attn_kernel<false, true> : (const void*)attn_kernel<false, false>);
+  const int lds = pair ? LDS_PAIR_BYTES : LDS_BYTES;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  if (p.needs_mask)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p);
-  else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p);
+  const dim3 grid((unsigned)nwg), block(NT);
+  if (p.needs_mask) {
+    if (pair) hipLaunchKernelGGL((attn_kernel<true, true>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((attn_kernel<true, false>), grid, block, lds, s, p);
+  } else {
+    if (pair) hipLaunchKernelGGL((attn_kernel<false, true>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((attn_kernel<false, false>), grid, block, lds, s, p);
+  }
   return hipGetLastError();
 }
 
