@@ -291,6 +291,59 @@ def summarize_counters(cfg_name, fetch_dir, write_dir, out_path, dram_dir=None):
     print(json.dumps(summary))
 
 
+ISSUE_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+                  "SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 1024      # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_issue(cfg_name, issue_dir, out_path):
+    """Per-SIMD issue figures of the attention launch from one rocprofv3 --pmc
+    pass over ISSUE_COUNTERS (counters summed over the chip by rocprofv3):
+    active cycles per XCD = GRBM_GUI_ACTIVE / 8 (their ratio to the dispatch's
+    duration is the average clock); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024
+    SIMDs over those cycles (32 per 32x32x16 bf16 MFMA); coexec the same for
+    SQ_VALU_MFMA_COEXEC_CYCLES; VALU active = 4 x SQ_ACTIVE_INST_VALU (counted
+    in quad-cycles) over the SIMD-cycles; instruction mix per MFMA."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(issue_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if ATTN_KERNEL not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Dispatch_Id"], {"_dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("no attention dispatch in %s" % issue_dir)
+    launches = []
+    for d in per.values():
+        cyc = d["GRBM_GUI_ACTIVE"] / N_XCD
+        mfma = d["SQ_INSTS_MFMA"]
+        launches.append({
+            "duration_ms": d["_dur"] * 1e3, "clock_ghz": cyc / d["_dur"] * 1e-9,
+            "waves": d["SQ_WAVES"], "mfma_insts": mfma,
+            "mfma_busy_frac": d["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cyc,
+            "mfma_busy_cycles_per_mfma": d["SQ_VALU_MFMA_BUSY_CYCLES"] / mfma,
+            "valu_mfma_coexec_frac": d["SQ_VALU_MFMA_COEXEC_CYCLES"] / N_SIMD / cyc,
+            "valu_active_frac": 4.0 * d["SQ_ACTIVE_INST_VALU"] / N_SIMD / cyc,
+            "valu_insts_per_mfma": (d["SQ_INSTS_VALU"] - mfma) / mfma,
+            "salu_insts_per_mfma": d["SQ_INSTS_SALU"] / mfma,
+        })
+    keys = [k for k in launches[0]]
+    mean = {k: float(np.mean([x[k] for x in launches])) for k in keys}
+    summary = {
+        "workload": cfg_name, "kernel": ATTN_KERNEL, "attn_source_sha": attn_source_hash(),
+        "history_path": history_path(workloads.CONFIGS[cfg_name]), "launches": len(launches),
+        "mean": mean,
+        "command": "rocprofv3 --pmc %s %s --output-format csv -d <issue_dir> -- "
+                   "python3 bench.py --config %s --counters-workload; python3 bench.py --config %s "
+                   "--summarize-issue <issue_dir>" % (ISSUE_COUNTERS, KERNEL_FILTER, cfg_name, cfg_name),
+    }
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary))
+
+
 TRAIN_METRIC = "packed-form attention forward+backward TFLOP/s; % of bf16 MFMA roofline"
 
 
@@ -760,6 +813,8 @@ def main():
                     help="one calibration copy + one attention call, for rocprofv3 --pmc")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="FETCH_DIR WRITE_DIR [DRAM_DIR]: rocprofv3 --pmc outputs to summarise")
+    ap.add_argument("--summarize-issue", metavar="DIR",
+                    help="a rocprofv3 --pmc output over the issue counters to summarise")
     ap.add_argument("--camera", action="store_true",
                     help="the per-latent-frame camera cross-attention instead")
     ap.add_argument("--linear", action="store_true",
@@ -778,6 +833,10 @@ def main():
         summarize_counters(args.config, d[0], d[1],
                            os.path.join(ROOT, "profiles", "attn_%s_counters.json" % args.config),
                            d[2] if len(d) == 3 else None)
+        return
+    if args.summarize_issue:
+        summarize_issue(args.config, args.summarize_issue,
+                        os.path.join(ROOT, "profiles", "attn_%s_issue.json" % args.config))
         return
     if args.counters_workload:
         counters_workload(args.config)
