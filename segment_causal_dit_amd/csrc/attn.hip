@@ -22,10 +22,14 @@
 //    loads (no staging registers); waves 0-3 stage, so each SIMD hosts one
 //    staging wave and one compute-only wave. Two schedules:
 //    - bf16 keys (a BF16 cache, or no history): two tiles per barrier,
-//      double buffered -- while tiles 2u and 2u+1 are computed from one
-//      128-key buffer, the loads of tiles 2u+2 and 2u+3 land in the other
+//      double buffered -- while tiles 2u and 2u+1 are computed from two
+//      tile slots, the loads of tiles 2u+2 and 2u+3 land in the other two
 //      (one barrier, one wait and one round of staging bookkeeping per 128
-//      keys);
+//      keys); the loop body exists once per slot pair, so every operand
+//      read takes its slot as an immediate offset; the loads are issued
+//      inside the iteration, not at its start, and history groups are
+//      found by a running (frame, row) position rather than a division and
+//      a slot lookup per tile;
 //    - an INT8 history: one tile per barrier, three tile buffers, loads two
 //      tiles ahead, and two staging areas for the codes and scales (the
 //      128-key buffers and the INT8 staging would not fit the 160 KB LDS);
@@ -57,7 +61,9 @@
 //    wave that loaded them, so the MFMA path is the same for both cache types;
 //  * online softmax in base 2 against a per-row reference max that moves
 //    only when needed: a tile's exponentials are taken against the current
-//    reference and summed (the row sum needs them anyway); only when that
+//    reference, rounded to bf16 as the PV operand and summed from those
+//    rounded values (dot products of the packed pairs with (1, 1)), so the
+//    row sum weighs every value exactly as the products do; only when that
 //    per-lane sum exceeds 2^12 (so some exponential might, or has
 //    overflowed) or the row has seen no visible key yet does the wave form
 //    the logits again, take the true tile max, rescale O and l and redo the
@@ -92,9 +98,12 @@ constexpr int RAW0 = NBUF * BUF_BYTES;           // two INT8 staging areas: code
 constexpr int RAW_KC = 0, RAW_VC = BN * D, RAW_S = 2 * BN * D;
 constexpr int RAW_BYTES = 2 * BN * D + NSTAGE * 256;   // codes + one 64-float scale block per wave
 constexpr int LDS_BYTES = RAW0 + 2 * RAW_BYTES;
-// pair schedule (bf16 keys only): two 64-key tiles per barrier, two 128-key buffers
-constexpr int PAIR_BYTES = 2 * BUF_BYTES;
-constexpr int LDS_PAIR_BYTES = 2 * PAIR_BYTES;
+// two-tile schedule (bf16 keys only): four tile slots (0 and 1 are computed
+// while 2 and 3 land, then the reverse); all K tiles lie in the first 64 KB
+// and all V tiles in the next, so that every operand read of any slot is a
+// per-lane base plus an immediate offset below 64 KB; then the four key tables
+constexpr int PK_OFF = 0, PV_OFF = 4 * TILE_BYTES, PI_OFF = 8 * TILE_BYTES;
+constexpr int LDS_PAIR_BYTES = PI_OFF + 4 * INFO_BYTES;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -247,7 +256,7 @@ __device__ inline int v_off(int r, int c) { return r * 256 + ((c ^ (5 * (r & 3))
 // INT8 rows).
 template <bool kInt8 = true>
 __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, int lane, int head,
-                                  char* buf, char* raw) {
+                                  char* kt, char* vt, char* raw) {
   const Group g = group_at(p, tl, w, head);
   if (!kInt8 || !tl.hist || !p.hist_int8) {
     if (g.lim >= RW - 1 && !g.generic) {
@@ -271,9 +280,9 @@ __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, in
 #pragma unroll
       for (int e = 0; e < RW / 4; ++e) {
         const uint32_t r = 4 * e + lrow;
-        char* dst = buf + (RW * w + 4 * e) * 256;
-        dload16_s(r * ks + ((pc ^ r) << 4), kb, dst + KOFF);
-        dload16_s(r * vs + ((pc ^ (5 * (lrow & 3))) << 4), vb, dst + VOFF);
+        const int dst = (RW * w + 4 * e) * 256;
+        dload16_s(r * ks + ((pc ^ r) << 4), kb, kt + dst);
+        dload16_s(r * vs + ((pc ^ (5 * (lrow & 3))) << 4), vb, vt + dst);
       }
       return 2 * (RW / 4);
     }
@@ -299,9 +308,9 @@ __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, in
     for (int e = 0; e < RW / 4; ++e) {
       const int row = RW * w + 4 * e + (lane >> 4);        // tile row of this lane's slot
       const int pc = lane & 15;                            // physical chunk in the LDS row
-      char* dst = buf + (RW * w + 4 * e) * 256;
-      dload16(krow[e] + ((pc ^ (row & 15)) << 4), dst + KOFF);
-      dload16(vrow[e] + ((pc ^ (5 * (row & 3))) << 4), dst + VOFF);
+      const int dst = (RW * w + 4 * e) * 256;
+      dload16(krow[e] + ((pc ^ (row & 15)) << 4), kt + dst);
+      dload16(vrow[e] + ((pc ^ (5 * (row & 3))) << 4), vt + dst);
     }
     return 2 * (RW / 4);
   } else {
@@ -323,6 +332,21 @@ __device__ inline int stage_issue(const AttnParams& p, const Tile& tl, int w, in
     }
     dload4((const void*)(sbase + (uint64_t)scr * 4), raw + RAW_S + w * 256);
     return 2 * (RW / 8) + 1;
+  }
+}
+
+// A whole history group (RW rows of one frame, 256-byte rows) from the
+// group's first cache row: the per-lane offsets depend only on the lane.
+__device__ inline void stage_hist_group(const AttnParams& p, int64_t row0, int w, int lane, char* kt, char* vt) {
+  const uint64_t kb = uniform_addr((const char*)p.hk + row0 * 256);
+  const uint64_t vb = uniform_addr((const char*)p.hv + row0 * 256);
+  const uint32_t lrow = lane >> 4, pc = lane & 15;
+#pragma unroll
+  for (int e = 0; e < RW / 4; ++e) {
+    const uint32_t r = 4 * e + lrow;
+    const int dst = (RW * w + 4 * e) * 256;
+    dload16_s(r * 256 + ((pc ^ r) << 4), kb, kt + dst);
+    dload16_s(r * 256 + ((pc ^ (5 * (lrow & 3))) << 4), vb, vt + dst);
   }
 }
 
@@ -410,17 +434,32 @@ struct RowState {
 // row max gives the same softmax: the final division uses the same reference.
 constexpr float kPLimit = 0x1p12f;
 
-__device__ inline float exp_sum(f32x16 (&s)[2], float c, float mc) {
+// Exponentials of one tile, packed to bf16 in the PV operand order (word
+// 4 ck + e of chunk ck holds accumulator values 8 (ck & 1) + 2 e and + 1 of
+// block ck >> 1), and their per-lane sum, taken from the packed values with
+// dot products against (1, 1) so that the row sum uses the same rounded
+// weights as the products.
+__device__ inline float exp_pack_sum(const f32x16 (&s)[2], float c, float mc, uint32_t (&pw)[16]) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int j = 0; j < 32; ++j) s[j >> 4][j & 15] = __builtin_amdgcn_exp2f(fmaf(s[j >> 4][j & 15], c, -mc));
-  float t[16];
+  for (int ck = 0; ck < 4; ++ck)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) t[j] = s[0][j] + s[1][j];
+    for (int e = 0; e < 4; ++e) {
+      const int j = 8 * (ck & 1) + 2 * e;
+      const float x0 = __builtin_amdgcn_exp2f(fmaf(s[ck >> 1][j], c, -mc));
+      const float x1 = __builtin_amdgcn_exp2f(fmaf(s[ck >> 1][j + 1], c, -mc));
+      pw[4 * ck + e] = pack_bf16(x0, x1);
+    }
+  float acc[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) t[j] = t[j] + t[j + 8];
+  for (int e = 0; e < 4; ++e) {
+    acc[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[e]), ones, 0.0f, false);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) t[j] = t[j] + t[j + 4];
-  return (t[0] + t[2]) + (t[1] + t[3]);
+    for (int ck = 1; ck < 4; ++ck)
+      acc[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[4 * ck + e]), ones, acc[e], false);
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 __device__ inline void mask_tile(f32x16 (&s)[2], const int* info, int qseg, int hh) {
@@ -439,9 +478,9 @@ __device__ inline void mask_tile(f32x16 (&s)[2], const int* info, int qseg, int 
 
 __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info, int qseg, int hh,
                                     float c, RowState& rs, f32x16 (&o)[4], float& ls,
-                                    const char* kbuf, const bf16x8 (&qf)[8], int lr) {
+                                    const char* kbuf, const bf16x8 (&qf)[8], int lr, uint32_t (&pw)[16]) {
   if (masked) mask_tile(s, info, qseg, hh);
-  ls = exp_sum(s, c, (rs.m == -INFINITY) ? 0.0f : rs.m * c);
+  ls = exp_pack_sum(s, c, (rs.m == -INFINITY) ? 0.0f : rs.m * c, pw);
   const bool need = !(ls <= kPLimit) || rs.m == -INFINITY;
   if (__builtin_amdgcn_ballot_w64(need)) {
     qk_tile(kbuf, qf, lr, hh, s);
@@ -467,7 +506,7 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-    ls = exp_sum(s, c, (rs.m == -INFINITY) ? 0.0f : rs.m * c);
+    ls = exp_pack_sum(s, c, (rs.m == -INFINITY) ? 0.0f : rs.m * c, pw);
   }
 }
 
@@ -477,7 +516,7 @@ __device__ inline void softmax_tile(f32x16 (&s)[2], bool masked, const int* info
 // base + j/4 at column d0 + 4 (j % 4); lane i then receives rows base..base+3
 // at column d0 + i, i.e. 4 keys of its own d. Two reads give the 8 keys the
 // P operand holds in this lane half (rows 16 ck + 4 hh + 0..3 and + 8..11).
-__device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane, int hh,
+__device__ inline void pv_tile(const char* vbuf, const uint32_t (&pw)[16], int lane, int hh,
                                f32x16 (&o)[4]) {
   // lane i of 16-lane group g reads row 16 ck + 4 hh + i / 4 and the row 8
   // further down, column 32 db + 16 (g & 1) + 4 (i % 4): chunk 4 db + hb with
@@ -491,11 +530,7 @@ __device__ inline void pv_tile(const char* vbuf, const f32x16 (&s)[2], int lane,
     // the four packed pairs go into a plain array first and into the vector
     // in one piece (writing vector elements one by one inside unrolled loops
     // has been seen to lose some of them in this compiler's output)
-    uint32_t wd[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      wd[e] = pack_bf16(s[ck >> 1][8 * (ck & 1) + 2 * e], s[ck >> 1][8 * (ck & 1) + 2 * e + 1]);
-    const u32x4 u = {wd[0], wd[1], wd[2], wd[3]};
+    const u32x4 u = {pw[4 * ck], pw[4 * ck + 1], pw[4 * ck + 2], pw[4 * ck + 3]};
     const bf16x8 pb = as_bf16x8(u);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -598,56 +633,98 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   const bool stager = w < NSTAGE;
   if constexpr (kPair) {
     // Two tiles per barrier, double buffered: during iteration u every wave
-    // computes tiles 2u and 2u+1 from buffer u % 2 while the staging waves'
-    // direct loads for tiles 2u+2 and 2u+3 land in the other buffer; at the
-    // end of the iteration they wait for those loads (issued a whole
-    // iteration earlier) and write the key tables of tiles that need a mask.
-    // The mask walk visits the tiles in ascending order, once each.
-    auto half = [&](const char* buf, bool masked) {
-      const int* info = (const int*)(buf + IOFF);
+    // computes tiles 2u and 2u+1 from slots 2 (u % 2) and + 1 while the
+    // staging waves' direct loads for tiles 2u+2 and 2u+3 land in the other
+    // two slots; at the end of the iteration the staging waves wait for those
+    // loads and write the key tables of tiles that need a mask. The mask walk
+    // visits the tiles in ascending order, once each.
+    //
+    // One tile: S^T, softmax, O^T += V^T P^T; `mid` runs between the S^T
+    // products and the softmax.
+    auto half = [&](int slot, bool masked, auto&& mid) __attribute__((always_inline)) {
+      const char* kb = smem + PK_OFF + slot * TILE_BYTES;
+      const int* info = (const int*)(smem + PI_OFF + slot * INFO_BYTES);
       f32x16 sc[2];
-      qk_tile(buf + KOFF, qf, lr, hh, sc);
+      qk_tile(kb, qf, lr, hh, sc);
+      mid();
       float ls;
-      softmax_tile(sc, masked, info, qseg, hh, c, rs, o, ls, buf + KOFF, qf, lr);
+      uint32_t pw[16];
+      softmax_tile(sc, masked, info, qseg, hh, c, rs, o, ls, kb, qf, lr, pw);
       rs.l += ls;
-      pv_tile(buf + VOFF, sc, lane, hh, o);
+      pv_tile(smem + PV_OFF + slot * TILE_BYTES, pw, lane, hh, o);
     };
+    // Staging waves walk the history in whole tiles with a running position
+    // of their group (frame hf, row hoff inside it, its cache slot hslot), so
+    // the slot list is read once per frame rather than once per tile. Tiles
+    // are issued in ascending order. Frames of a multiple of RW tokens only
+    // (a group then never straddles a frame); other tiles take the general path.
+    const bool hwalk = p.G % RW == 0;
+    const int full_hist_tiles = p.n_hist_rows / BN;
+    int hf = 0, hoff = RW * w, hslot = 0;
+    if (stager && hwalk && full_hist_tiles > 0) {
+      while (hoff >= p.G) { hoff -= p.G; ++hf; }
+      hslot = const_load(p.hist_slots + hf);
+    }
+    auto issue = [&](int t, int slot) __attribute__((always_inline)) {
+      char* const kt = smem + PK_OFF + slot * TILE_BYTES;
+      char* const vt = smem + PV_OFF + slot * TILE_BYTES;
+      if (hwalk && t < full_hist_tiles) {
+        stage_hist_group(p, ((int64_t)hslot * p.n_heads + head) * p.G + hoff, w, lane, kt, vt);
+        hoff += BN;
+        if (hoff >= p.G) {
+          do { hoff -= p.G; ++hf; } while (hoff >= p.G);
+          if (t + 1 < full_hist_tiles) hslot = const_load(p.hist_slots + hf);
+        }
+      } else {
+        stage_issue<false>(p, tile_at(p, t, cur_end), w, lane, head, kt, vt, nullptr);
+      }
+    };
+    auto info_at = [&](int slot) __attribute__((always_inline)) { return (int*)(smem + PI_OFF + slot * INFO_BYTES); };
     bool m0t = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
     const int s0 = mw.kseg.s;
     bool m1t = n_tiles > 1 && tile_masked<kSeg>(p, tile_at(p, 1, cur_end), mw);
     const int s1 = mw.kseg.s;
     if (stager) {
-      stage_issue<false>(p, tile_at(p, 0, cur_end), w, lane, head, smem, nullptr);
-      if (n_tiles > 1) stage_issue<false>(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, nullptr);
+      issue(0, 0);
+      if (n_tiles > 1) issue(1, 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (m0t) store_info<kSeg>(p, tile_at(p, 0, cur_end), tid, (int*)(smem + IOFF), s0);
-      if (m1t) store_info<kSeg>(p, tile_at(p, 1, cur_end), tid, (int*)(smem + BUF_BYTES + IOFF), s1);
+      if (m0t) store_info<kSeg>(p, tile_at(p, 0, cur_end), tid, info_at(0), s0);
+      if (m1t) store_info<kSeg>(p, tile_at(p, 1, cur_end), tid, info_at(1), s1);
     }
     __syncthreads();
     const int n_pairs = (n_tiles + 1) >> 1;
-    for (int u = 0; u < n_pairs; ++u) {
-      char* const cur = smem + (u & 1) * PAIR_BYTES;
-      char* const nxt = smem + ((u & 1) ^ 1) * PAIR_BYTES;
+    // the loop body is instantiated once per slot parity, so that every LDS
+    // operand address is a loop-invariant per-lane base plus an immediate
+    auto pair_iter = [&](int u, int cs) __attribute__((always_inline)) {
+      const int ns = 2 - cs;
       __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
       const int t0 = 2 * u;
-      if (stager && t0 + 2 < n_tiles) {
-        stage_issue<false>(p, tile_at(p, t0 + 2, cur_end), w, lane, head, nxt, nullptr);
-        if (t0 + 3 < n_tiles) stage_issue<false>(p, tile_at(p, t0 + 3, cur_end), w, lane, head, nxt + BUF_BYTES, nullptr);
-      }
-      half(cur, m0t);
-      if (t0 + 1 < n_tiles) half(cur + BUF_BYTES, m1t);
+      // The staging waves issue tile t0+2's loads after the first tile and
+      // tile t0+3's between the second tile's S^T products and its softmax:
+      // issued all at the start of the iteration (or right after the first
+      // tile's S^T products) they held the staging waves back, and every
+      // wave waits for those at the barrier.
+      auto none = [&]() __attribute__((always_inline)) {};
+      auto second = [&]() __attribute__((always_inline)) { if (stager && t0 + 3 < n_tiles) issue(t0 + 3, ns + 1); };
+      half(cs, m0t, none);
+      if (stager && t0 + 2 < n_tiles) issue(t0 + 2, ns);
+      if (t0 + 1 < n_tiles) half(cs + 1, m1t, second);
       const bool n0 = t0 + 2 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t0 + 2, cur_end), mw);
       const int sg0 = mw.kseg.s;
       const bool n1 = t0 + 3 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t0 + 3, cur_end), mw);
       const int sg1 = mw.kseg.s;
       if (stager && t0 + 2 < n_tiles) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (n0) store_info<kSeg>(p, tile_at(p, t0 + 2, cur_end), tid, (int*)(nxt + IOFF), sg0);
-        if (n1) store_info<kSeg>(p, tile_at(p, t0 + 3, cur_end), tid, (int*)(nxt + BUF_BYTES + IOFF), sg1);
+        if (n0) store_info<kSeg>(p, tile_at(p, t0 + 2, cur_end), tid, info_at(ns), sg0);
+        if (n1) store_info<kSeg>(p, tile_at(p, t0 + 3, cur_end), tid, info_at(ns + 1), sg1);
       }
       __syncthreads();
       m0t = n0;
       m1t = n1;
+    };
+    for (int u = 0; u < n_pairs; u += 2) {
+      pair_iter(u, 0);
+      if (u + 1 < n_pairs) pair_iter(u + 1, 2);
     }
   } else {
     // One tile per barrier (an INT8 history), loads two tiles ahead: during
@@ -662,9 +739,9 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     bool mt = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
     if (stager) {
       const Tile t0 = tile_at(p, 0, cur_end);
-      stage_issue(p, t0, w, lane, head, smem, raw0);
+      stage_issue(p, t0, w, lane, head, smem + KOFF, smem + VOFF, raw0);
       stage_finish<kSeg>(p, t0, w, lane, tid, smem, raw0, 0, mt, mw.kseg.s);
-      if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES, raw1);
+      if (n_tiles > 1) stage_issue(p, tile_at(p, 1, cur_end), w, lane, head, smem + BUF_BYTES + KOFF, smem + BUF_BYTES + VOFF, raw1);
     }
     __syncthreads();
     int bc = 0;
@@ -681,13 +758,14 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
       __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
       int issued = 0;
       if (stager && t + 2 < n_tiles)
-        issued = stage_issue(p, tile_at(p, t + 2, cur_end), w, lane, head, nx2, (t & 1) ? raw1 : raw0);
+        issued = stage_issue(p, tile_at(p, t + 2, cur_end), w, lane, head, nx2 + KOFF, nx2 + VOFF, (t & 1) ? raw1 : raw0);
       f32x16 sc[2];
       qk_tile(cur + KOFF, qf, lr, hh, sc);
       float ls;
-      softmax_tile(sc, mt, info, qseg, hh, c, rs, o, ls, cur + KOFF, qf, lr);
+      uint32_t pw[16];
+      softmax_tile(sc, mt, info, qseg, hh, c, rs, o, ls, cur + KOFF, qf, lr, pw);
       rs.l += ls;
-      pv_tile(cur + VOFF, sc, lane, hh, o);
+      pv_tile(cur + VOFF, pw, lane, hh, o);
       const bool mt_next = t + 1 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t + 1, cur_end), mw);
       if (stager && t + 1 < n_tiles)
         stage_finish<kSeg>(p, tile_at(p, t + 1, cur_end), w, lane, tid, nx1, (t & 1) ? raw0 : raw1, issued, mt_next,
