@@ -21,12 +21,17 @@ SEGC_OK, SEGC_EINVAL, SEGC_EUNSUPPORTED, SEGC_EHIP = 0, 1, 2, 3
 SEGC_BF16, SEGC_INT8 = 0, 1
 HEAD_DIM = 128
 MAX_SEG = 16
+ABI_VERSION = (1 << 16) | 8      # SEGC_ABI_VERSION of the header these bindings mirror
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         "libsegcausal.so is not built; run `python -m segment_causal_dit_amd.build` "
         "(or __graft_entry__.build()) first")
 _lib = ctypes.CDLL(LIB_PATH)
+_lib.segcausal_abi_version.restype = ctypes.c_int
+if _lib.segcausal_abi_version() != ABI_VERSION:
+    raise ImportError("%s has ABI version 0x%x, these bindings expect 0x%x; rebuild it"
+                      % (LIB_PATH, _lib.segcausal_abi_version(), ABI_VERSION))
 
 _i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 _pi32 = ctypes.POINTER(ctypes.c_int32)

@@ -32,6 +32,7 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     m = re.search(r"#define SEGC_ABI_VERSION \(\(1 << 16\) \| (\d+)\)", open(HEADER).read())
     assert m and lib.segcausal_abi_version() == (1 << 16) | int(m.group(1))
+    assert sc.ABI_VERSION == (1 << 16) | int(m.group(1))     # the binding checks it at import
 
 
 def test_window_select_matches_oracle():
