@@ -30,7 +30,9 @@
 //    dV^T += dO^T P and dK^T += Q^T dS; the two waves of a key group add
 //    their partial dK and dV through LDS at the end.
 // 64-row tiles are staged through LDS, double buffered, by direct global->LDS
-// loads issued from inline assembly and awaited explicitly once per tile.
+// loads issued from inline assembly and awaited explicitly once per tile (the
+// dK/dV kernel issues the next tile's loads after the current tile's S and dP
+// products, and fetches its lse and delta in the same place).
 // Chunk c of tile row r sits at c ^ (((r & 3) << 2) | ((r >> 2) & 3)): every
 // read by rows (16 consecutive rows, one chunk) and every transposing read
 // (4 aligned chunks of 4 aligned rows) touches distinct bank groups. Tile
@@ -165,11 +167,17 @@ __device__ inline void rows_x_frag(const char* tile, const bf16x8 (&f)[8], int l
 // as bf16 B operands over the tile rows: chunk ck holds rows 16 ck + 4 hh +
 // 0..3 in slots 0-3 and 16 ck + 8 + 4 hh + 0..3 in slots 4-7.
 __device__ inline void pack_rows(const f32x16 (&x)[2], u32x4 (&pk)[4]) {
+  // packed words go into a plain array first and into each vector in one
+  // piece (element-wise writes of vectors inside unrolled loops have lost
+  // values in this compiler's output)
 #pragma unroll
-  for (int ck = 0; ck < 4; ++ck)
+  for (int ck = 0; ck < 4; ++ck) {
+    uint32_t wd[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      pk[ck][e] = pack_bf16(x[ck >> 1][8 * (ck & 1) + 2 * e], x[ck >> 1][8 * (ck & 1) + 2 * e + 1]);
+      wd[e] = pack_bf16(x[ck >> 1][8 * (ck & 1) + 2 * e], x[ck >> 1][8 * (ck & 1) + 2 * e + 1]);
+    pk[ck] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+  }
 }
 
 // out[db] += T^T[32 db + ..][rows] pk[rows][lanes]: the tile's columns as
@@ -472,6 +480,29 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
       ((int*)tb)[2 * BN + tid] = row_segment(p, sg, q0, BN, r);
     }
   };
+  // The next tile's lse and delta are fetched during an iteration, into
+  // registers of the lanes that write the table, and stored at its end: a
+  // fetch at the end would hold every wave at the barrier for a memory round
+  // trip.
+  float nl = 0.0f, nd = 0.0f;
+  auto fetch_next = [&](int q0) {
+    if (tid < BN) {
+      const int r = min(q0 + tid, p.n - 1);
+      nl = p.lse[(int64_t)head * p.n + r];
+      nd = p.delta[(int64_t)head * p.n + r];
+    }
+  };
+  auto finish_next = [&](int q0, char* buf, int sg) {
+    dload_wait();
+    if (tid < BN) {
+      const int r = q0 + tid;
+      const bool ok = r < p.n;
+      float* tb = (float*)(buf + TOFF);
+      tb[tid] = ok ? nl * kLog2e : INFINITY;
+      tb[BN + tid] = ok ? nd : 0.0f;
+      ((int*)tb)[2 * BN + tid] = row_segment(p, sg, q0, BN, r);
+    }
+  };
   // the tile needs the mask unless every key here is video of a segment no
   // later than every query in it
   SegWalk qw;
@@ -491,9 +522,6 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
     char* const nxt = stage + ((t + 1) & 1) * BUF_BYTES;
     const bool has_next = t + 1 < n_qt;
     const int q0 = q_begin + t * BN;
-    if (has_next)
-      stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt + AOFF,
-                          nxt + BOFF);
     // S = Q K^T and dP = dO V^T over this wave's 32 queries and 32 keys:
     // queries in the accumulator rows, keys across lanes
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -507,6 +535,13 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
       const bf16x8 bv = *(const bf16x8*)(vtile_l + t_off(lr, 2 * dt + hh));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
+    }
+    // the next tile's loads go out after this tile's S and dP products (at
+    // the start of the iteration, or later, they measured slower)
+    if (has_next) {
+      stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt + AOFF,
+                          nxt + BOFF);
+      fetch_next(q0 + BN);
     }
     const float* tb = (const float*)(cur + TOFF);
     f32x16 pm, ds;
@@ -526,19 +561,23 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
     }
     u32x4 pkp[2], pkd[2];
 #pragma unroll
-    for (int ck = 0; ck < 2; ++ck)
+    for (int ck = 0; ck < 2; ++ck) {
+      uint32_t wp[4], wd[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pkp[ck][e] = pack_bf16(pm[8 * ck + 2 * e], pm[8 * ck + 2 * e + 1]);
-        pkd[ck][e] = pack_bf16(ds[8 * ck + 2 * e], ds[8 * ck + 2 * e + 1]);
+        wp[e] = pack_bf16(pm[8 * ck + 2 * e], pm[8 * ck + 2 * e + 1]);
+        wd[e] = pack_bf16(ds[8 * ck + 2 * e], ds[8 * ck + 2 * e + 1]);
       }
+      pkp[ck] = u32x4{wp[0], wp[1], wp[2], wp[3]};
+      pkd[ck] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+    }
     tileT_x_packed32(da, 32 * qh, pkp, lane, hh, dvacc);   // dV^T += dO^T P
     tileT_x_packed32(qa, 32 * qh, pkd, lane, hh, dkacc);   // dK^T += Q^T dS
     bool masked_next = false;
     if (has_next) {
       const int qs = qw.at(p, q0 + BN);
       masked_next = tile_masked(qs);
-      finish(q0 + BN, nxt, qs);
+      finish_next(q0 + BN, nxt, qs);
     }
     __syncthreads();
     masked = masked_next;
