@@ -375,9 +375,10 @@ __device__ inline void convert_group(const char* codes, const float* scales, cha
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    u32x4 o;
+    uint32_t wd[4];                      // plain array first, vector in one piece
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = pack_bf16(f[8 * e + 2 * k], f[8 * e + 2 * k + 1]);
+    for (int k = 0; k < 4; ++k) wd[k] = pack_bf16(f[8 * e + 2 * k], f[8 * e + 2 * k + 1]);
+    const u32x4 o = {wd[0], wd[1], wd[2], wd[3]};
     const int cc = 4 * q + e;
     *(u32x4*)(tile + (IS_V ? v_off(row, cc) : k_off(row, cc))) = o;
   }

@@ -116,10 +116,10 @@ __global__ __launch_bounds__(kThreads) void camera_attn_kernel(CamParams p) {
     m = mx;
   }
   const float inv = 1.0f / l;
-  u32x4 o;
+  uint32_t wd[4];                        // plain array first, vector in one piece
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-  *dst = o;
+  for (int e = 0; e < 4; ++e) wd[e] = pack_bf16(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+  *dst = u32x4{wd[0], wd[1], wd[2], wd[3]};
 }
 
 }  // namespace
