@@ -45,6 +45,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def bwd_source_hash():
+    with open(os.path.join(ROOT, "segment_causal_dit_amd", "csrc", "attn_bwd.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
 def attn_source_hash():
     with open(os.path.join(ROOT, "segment_causal_dit_amd", "csrc", "attn.hip"), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -296,7 +301,7 @@ ISSUE_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA
 N_XCD, N_SIMD = 8, 1024      # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 
-def summarize_issue(cfg_name, issue_dir, out_path):
+def summarize_issue(cfg_name, issue_dir, out_path, kernel=ATTN_KERNEL, workload_cmd=None):
     """Per-SIMD issue figures of the attention launch from one rocprofv3 --pmc
     pass over ISSUE_COUNTERS (counters summed over the chip by rocprofv3):
     active cycles per XCD = GRBM_GUI_ACTIVE / 8 (their ratio to the dispatch's
@@ -309,12 +314,12 @@ def summarize_issue(cfg_name, issue_dir, out_path):
     per = {}
     for f in glob.glob(os.path.join(issue_dir, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            if ATTN_KERNEL not in r["Kernel_Name"]:
+            if kernel not in r["Kernel_Name"]:
                 continue
             d = per.setdefault(r["Dispatch_Id"], {"_dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     if not per:
-        raise SystemExit("no attention dispatch in %s" % issue_dir)
+        raise SystemExit("no %s dispatch in %s" % (kernel, issue_dir))
     launches = []
     for d in per.values():
         cyc = d["GRBM_GUI_ACTIVE"] / N_XCD
@@ -331,13 +336,20 @@ def summarize_issue(cfg_name, issue_dir, out_path):
         })
     keys = [k for k in launches[0]]
     mean = {k: float(np.mean([x[k] for x in launches])) for k in keys}
+    if workload_cmd is None:
+        workload_cmd = "python3 bench.py --config %s --counters-workload" % cfg_name
+        summarize_cmd = "python3 bench.py --config %s --summarize-issue <issue_dir>" % cfg_name
+        filt = KERNEL_FILTER
+    else:
+        summarize_cmd = "python3 bench.py --train --summarize-issue <issue_dir> --issue-kernel %s" % kernel
+        filt = "--kernel-include-regex %s" % kernel
     summary = {
-        "workload": cfg_name, "kernel": ATTN_KERNEL, "attn_source_sha": attn_source_hash(),
-        "history_path": history_path(workloads.CONFIGS[cfg_name]), "launches": len(launches),
-        "mean": mean,
-        "command": "rocprofv3 --pmc %s %s --output-format csv -d <issue_dir> -- "
-                   "python3 bench.py --config %s --counters-workload; python3 bench.py --config %s "
-                   "--summarize-issue <issue_dir>" % (ISSUE_COUNTERS, KERNEL_FILTER, cfg_name, cfg_name),
+        "workload": cfg_name, "kernel": kernel,
+        "source_sha": attn_source_hash() if kernel == ATTN_KERNEL else bwd_source_hash(),
+        "history_path": history_path(workloads.CONFIGS[cfg_name]) if cfg_name in workloads.CONFIGS else None,
+        "launches": len(launches), "mean": mean,
+        "command": "rocprofv3 --pmc %s %s --output-format csv -d <issue_dir> -- %s; %s"
+                   % (ISSUE_COUNTERS, filt, workload_cmd, summarize_cmd),
     }
     with open(out_path, "w") as f:
         json.dump(summary, f, indent=1)
@@ -815,6 +827,8 @@ def main():
                     help="FETCH_DIR WRITE_DIR [DRAM_DIR]: rocprofv3 --pmc outputs to summarise")
     ap.add_argument("--summarize-issue", metavar="DIR",
                     help="a rocprofv3 --pmc output over the issue counters to summarise")
+    ap.add_argument("--issue-kernel", default=ATTN_KERNEL,
+                    help="kernel whose dispatches --summarize-issue reads (with --train: dq_kernel, dkdv_kernel)")
     ap.add_argument("--camera", action="store_true",
                     help="the per-latent-frame camera cross-attention instead")
     ap.add_argument("--linear", action="store_true",
@@ -835,8 +849,14 @@ def main():
                            d[2] if len(d) == 3 else None)
         return
     if args.summarize_issue:
-        summarize_issue(args.config, args.summarize_issue,
-                        os.path.join(ROOT, "profiles", "attn_%s_issue.json" % args.config))
+        if args.train:
+            summarize_issue("train13", args.summarize_issue,
+                            os.path.join(ROOT, "profiles", "%s_train13_issue.json" % args.issue_kernel),
+                            kernel=args.issue_kernel,
+                            workload_cmd="python3 bench.py --train --steps 1 --warmup 0 --no-cpu-baseline")
+        else:
+            summarize_issue(args.config, args.summarize_issue,
+                            os.path.join(ROOT, "profiles", "attn_%s_issue.json" % args.config))
         return
     if args.counters_workload:
         counters_workload(args.config)
