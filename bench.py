@@ -135,9 +135,11 @@ def config_rates(names, reps=20):
                 deq_ms = a.elapsed_time(b)
                 cache, hist = win, torch.arange(len(hist), dtype=torch.int32, device=dev)
         o = torch.empty_like(q)
+        ws = attn_workspace(sc, cfg.n_cur, cfg.n_heads, inp.segments, hist, cache, dev)
 
         def call():
-            sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist, out=o)
+            sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist, out=o,
+                                    workspace=ws)
 
         for _ in range(3):
             call()
@@ -163,6 +165,15 @@ def config_rates(names, reps=20):
         del q, k, v, o, cache, hist
         torch.cuda.empty_cache()
     return out
+
+
+def attn_workspace(sc, n_cur, n_heads, segments, hist, cache, dev):
+    """The attention's split workspace, allocated once outside the timed
+    region (None when the call would not split)."""
+    import torch
+    n_hist = 0 if hist is None else int(hist.numel())
+    need = sc.attn_workspace_bytes(n_cur, n_heads, segments, n_hist, cache if n_hist else None)
+    return torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
 
 
 def cpu_baseline(cfg, inp, n_rows=512):
@@ -226,8 +237,9 @@ def counters_workload(cfg_name):
             win = sc.KVCache(len(hist), cfg.n_heads, cfg.tokens_per_frame, "bf16", dev)
             sc.kv_window_dequant(cache, hist, win)
             cache, hist = win, torch.arange(len(hist), dtype=torch.int32, device=dev)
+    ws = attn_workspace(sc, cfg.n_cur, cfg.n_heads, inp.segments, hist, cache, dev)
     torch.cuda.synchronize()
-    sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist)
+    sc.segcausal_joint_attn(q, k, v, inp.segments, cfg.sm_scale, cache=cache, hist_slots=hist, workspace=ws)
     torch.cuda.synchronize()
     log("counters workload done")
 
@@ -540,8 +552,11 @@ def archive_bench(args):
         b.record(stream)
         return a, b
 
+    ws = attn_workspace(sc, cfg.n_cur, cfg.n_heads, segs, hist, cache, dev)
+
     def attn():
-        sc.segcausal_joint_attn(q, k, v, segs, cfg.sm_scale, cache=cache, hist_slots=hist, out=out)
+        sc.segcausal_joint_attn(q, k, v, segs, cfg.sm_scale, cache=cache, hist_slots=hist, out=out,
+                                workspace=ws)
 
     def fetch():
         sc.kv_archive_fetch(arch, fetch_frames, cache, fetch_slots, stream=copy_stream)
@@ -909,6 +924,10 @@ def main():
         del hk
     expand = cache is not None and cfg.cache_dtype == "int8" and args.int8_attn == "window"
     win = sc.KVCache(min(cfg.window, n_hist_frames), h, g, "bf16", dev) if expand else None
+    n_win = len(sc.window_select(cache.slot_t[:n_hist_frames], cfg.window)) if cache else 0
+    ws = attn_workspace(sc, cfg.n_cur, h, [(0, tl, seg.text_valid)],
+                        torch.zeros(n_win, dtype=torch.int32) if n_win else None,
+                        win if expand else cache, dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -935,7 +954,7 @@ def main():
                 rec("dequant", lambda: sc.kv_window_dequant(cache, hist, win))
             rec("attn", lambda: sc.segcausal_joint_attn(q, k, v, [(0, tl, seg.text_valid)],
                                                         cfg.sm_scale, cache=acache,
-                                                        hist_slots=ahist, out=out))
+                                                        hist_slots=ahist, out=out, workspace=ws))
         if cache is not None and cfg.append:
             rec("append", lambda: sc.kv_cache_append(cache, n_hist_frames, k[tl:], v[tl:]))
 
@@ -987,7 +1006,7 @@ def main():
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             sc.segcausal_joint_attn(q, k, v, [(0, tl, seg.text_valid)], cfg.sm_scale, cache=cache,
-                                    hist_slots=hist, out=out)
+                                    hist_slots=hist, out=out, workspace=None)
             b.record(stream)
             fused.append((a, b))
         torch.cuda.synchronize()

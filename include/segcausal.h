@@ -319,6 +319,9 @@ typedef struct segc_attn_args {
   const int32_t* hist_slots;       /* device int32 [n_hist], slot indices (e.g. from window_select) */
   int32_t n_hist;                  /* number of history frames, 0 = none */
   float   sm_scale;                /* > 0, e.g. 1/sqrt(128) */
+  int32_t reserved2;               /* must be 0 */
+  void*   workspace;               /* optional device scratch (see below); NULL = none */
+  int64_t workspace_bytes;         /* its size in bytes */
 } segc_attn_args;
 
 /*
@@ -335,6 +338,25 @@ typedef struct segc_attn_args {
  *   read on the device and must lie in [0, n_slots) (a precondition).
  */
 int segcausal_joint_attn(const segc_attn_args* args, void* stream);
+
+/*
+ * Bytes of device workspace with which segcausal_joint_attn(args) splits its
+ * last partial round of workgroups: the grid has one workgroup per (head,
+ * 256-query tile); when their number is not a multiple of the device's
+ * compute units, the last round would leave units idle, so those tiles are
+ * split by key range into several workgroups each, whose partial results
+ * (fp32 O, row max, row sum) land in the workspace and are merged by lse in
+ * one more launch. Returns 0 when the call would not split (it needs one
+ * unpadded segment, bf16 keys, at least four whole rounds before the partial
+ * one, and a split that pays by a cost model), -1 on a NULL args. n_cu > 0 gives the compute-unit count; 0 asks the current device
+ * (-1 if that fails). The result depends only on n_cur, n_heads, the segment
+ * tables, n_hist, the cache's tokens_per_frame and dtype, and n_cu.
+ * With workspace NULL the call does not split. A non-NULL workspace must be
+ * 16-byte aligned and hold at least this many bytes (else EINVAL); it is
+ * caller-owned device memory, written and read on the call's stream, so two
+ * calls in flight at once need two workspaces.
+ */
+int64_t segcausal_joint_attn_workspace_bytes(const segc_attn_args* args, int32_t n_cu);
 
 /*
  * segcausal_joint_attn_bwd -- gradients of segcausal_joint_attn in the packed
@@ -420,7 +442,7 @@ const char* segcausal_last_error(void);
 
 /* ABI version of this header, (major << 16) | minor. */
 int segcausal_abi_version(void);
-#define SEGC_ABI_VERSION ((1 << 16) | 8)
+#define SEGC_ABI_VERSION ((1 << 16) | 9)
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ SEGC_OK, SEGC_EINVAL, SEGC_EUNSUPPORTED, SEGC_EHIP = 0, 1, 2, 3
 SEGC_BF16, SEGC_INT8 = 0, 1
 HEAD_DIM = 128
 MAX_SEG = 16
-ABI_VERSION = (1 << 16) | 8      # SEGC_ABI_VERSION of the header these bindings mirror
+ABI_VERSION = (1 << 16) | 9      # SEGC_ABI_VERSION of the header these bindings mirror
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -53,7 +53,8 @@ class SegcAttnArgs(ctypes.Structure):
                 ("n_seg", _i32), ("reserved", _i32),
                 ("seg_start", _pi32), ("seg_text_len", _pi32), ("seg_text_valid", _pi32),
                 ("cache", ctypes.POINTER(SegcCache)), ("hist_slots", _vp),
-                ("n_hist", _i32), ("sm_scale", _f32)]
+                ("n_hist", _i32), ("sm_scale", _f32), ("reserved2", _i32),
+                ("workspace", _vp), ("workspace_bytes", _i64)]
 
 
 class SegcAttnBwdArgs(ctypes.Structure):
@@ -85,6 +86,8 @@ _lib.camera_cross_attn.argtypes = [ctypes.POINTER(SegcCameraArgs), _vp]
 _lib.kv_archive_fetch.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.kv_archive_store.argtypes = [ctypes.POINTER(SegcCache), _pi32, ctypes.POINTER(SegcCache), _pi32, _i32, _vp]
 _lib.segcausal_joint_attn.argtypes = [ctypes.POINTER(SegcAttnArgs), _vp]
+_lib.segcausal_joint_attn_workspace_bytes.argtypes = [ctypes.POINTER(SegcAttnArgs), _i32]
+_lib.segcausal_joint_attn_workspace_bytes.restype = _i64
 _lib.segcausal_joint_attn_bwd.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
 _lib.segcausal_joint_attn_bwd_noalloc.argtypes = [ctypes.POINTER(SegcAttnBwdArgs), _vp]
 _lib.segcausal_last_error.restype = ctypes.c_char_p
@@ -95,8 +98,8 @@ for _f in ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_selec
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("rope3d_apply", "kv_cache_append", "kv_window_dequant", "window_select",
-           "segcausal_joint_attn", "segcausal_joint_attn_bwd", "segcausal_joint_attn_bwd_noalloc",
-           "kv_archive_fetch", "kv_archive_store",
+           "segcausal_joint_attn", "segcausal_joint_attn_workspace_bytes", "segcausal_joint_attn_bwd",
+           "segcausal_joint_attn_bwd_noalloc", "kv_archive_fetch", "kv_archive_store",
            "w8a16_linear", "camera_cross_attn", "segcausal_last_error", "segcausal_abi_version")
 
 
@@ -329,13 +332,16 @@ def window_select(slot_t, budget):
 
 
 def segcausal_joint_attn(q, k, v, segments, sm_scale, cache=None, hist_slots=None, out=None,
-                         lse=None, stream=None):
+                         lse=None, stream=None, workspace="auto"):
     """Segment-wise causal joint attention.
 
     q, k, v    : bf16 [n_cur, H, 128] (video rows already rotated)
     segments   : list of (start, text_len, text_valid)
     cache      : KVCache or None; hist_slots: device int32 tensor [n_hist]
     out        : optional bf16 [n_cur, H, 128]; lse: optional fp32 [H, n_cur]
+    workspace  : device tensor for splitting the launch's last partial round
+                 (attn_workspace_bytes gives its size); "auto" allocates one
+                 when the call would split, None never splits
     """
     pq, qst, qsh = _rows(q, "q")
     pk, kst, ksh = _rows(k, "k")
@@ -368,9 +374,36 @@ def segcausal_joint_attn(q, k, v, segments, sm_scale, cache=None, hist_slots=Non
     args = SegcAttnArgs(pq, pk, pv, po, qst, qsh, kst, ksh, vst, vsh, ost, osh,
                         lse.data_ptr() if lse is not None else None, n_cur, nh, HEAD_DIM,
                         len(segments), 0, seg_start, tl, tv, cache_ptr, hs_ptr, n_hist,
-                        float(sm_scale))
+                        float(sm_scale), 0, None, 0)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be a tensor, None or 'auto'")
+        need = _lib.segcausal_joint_attn_workspace_bytes(ctypes.byref(args), 0)
+        if need < 0:
+            raise SegcError(SEGC_EHIP, "segcausal_joint_attn_workspace_bytes failed")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need > 0 else None
+    if workspace is not None:
+        _on_gpu(q.device, workspace=workspace)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.segcausal_joint_attn(ctypes.byref(args), _stream(stream)))
     return out
+
+
+def attn_workspace_bytes(n_cur, n_heads, segments, n_hist=0, cache=None, n_cu=0):
+    """Bytes of workspace with which segcausal_joint_attn splits its last
+    partial round for this shape (0: it would not split); n_cu = 0 asks the
+    current device for its compute-unit count."""
+    seg_start, tl, tv = _segment_tables(segments, n_cur)
+    args = SegcAttnArgs()
+    args.n_cur, args.n_heads, args.head_dim, args.n_seg = n_cur, n_heads, HEAD_DIM, len(segments)
+    args.seg_start, args.seg_text_len, args.seg_text_valid = seg_start, tl, tv
+    args.n_hist = n_hist
+    if cache is not None:
+        args.cache = ctypes.pointer(cache.desc)
+    return _lib.segcausal_joint_attn_workspace_bytes(ctypes.byref(args), n_cu)
 
 
 def _segment_tables(segments, n):

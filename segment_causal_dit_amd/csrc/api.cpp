@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -33,6 +34,26 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute units of the current device, looked up once per device.
+int device_cu_count(int* n_cu) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SEGC_EINVAL, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute");
+    cache[dev] = v;
+  }
+  *n_cu = cache[dev];
+  return SEGC_OK;
+}
 
 // Strides are multiples of 8 elements (16-byte rows) and below
 // SEGC_MAX_STRIDE: the kernels form a row's offset inside a staged group of at
@@ -412,6 +433,8 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
   if (a->n_cur * a->n_heads >= ((int64_t)1 << 31)) return fail(SEGC_EINVAL, "n_cur x n_heads must be below 2^31");
   if (!(a->sm_scale > 0.0f) || !std::isfinite(a->sm_scale))
     return fail(SEGC_EINVAL, "sm_scale must be finite and > 0");
+  if (a->reserved != 0 || a->reserved2 != 0) return fail(SEGC_EINVAL, "reserved fields must be 0");
+  if (a->workspace_bytes < 0) return fail(SEGC_EINVAL, "workspace_bytes < 0");
   if (!strides_ok(a->q_stride_tok, a->q_stride_head) || !strides_ok(a->k_stride_tok, a->k_stride_head) ||
       !strides_ok(a->v_stride_tok, a->v_stride_head) || !strides_ok(a->o_stride_tok, a->o_stride_head))
     return fail(SEGC_EINVAL, "strides must be non-negative multiples of 8 elements below 2^26");
@@ -483,7 +506,41 @@ int segcausal_joint_attn(const segc_attn_args* a, void* stream) {
   p.needs_mask = needs_mask;
   p.sm_scale = a->sm_scale;
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  if (a->workspace) {
+    if (!aligned16(a->workspace)) return fail(SEGC_EINVAL, "workspace must be 16-byte aligned");
+    int n_cu = 0;
+    rc = device_cu_count(&n_cu);
+    if (rc) return rc;
+    const int64_t need = segc::attn_split_plan(p, n_cu);
+    if (a->workspace_bytes < need)
+      return fail(SEGC_EINVAL, "workspace holds %lld bytes, this call needs %lld", (long long)a->workspace_bytes,
+                  (long long)need);
+    p.ws = (float*)a->workspace;
+  } else {
+    segc::attn_split_plan(p, 0);             // no workspace: no split
+  }
   return hip_status(segc::launch_attn(p, (hipStream_t)stream), "segcausal_joint_attn launch");
+}
+
+int64_t segcausal_joint_attn_workspace_bytes(const segc_attn_args* a, int32_t n_cu) {
+  if (!a) return -1;
+  if (a->n_seg < 1 || a->n_seg > SEGC_MAX_SEG || a->n_cur < 0 || a->n_cur > (int64_t)1 << 30 ||
+      a->n_heads < 1 || a->n_heads > 1024 || !a->seg_text_len || !a->seg_text_valid)
+    return -1;
+  segc::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.n_cur = (int32_t)a->n_cur;
+  p.n_heads = a->n_heads;
+  bool needs_mask = a->n_seg > 1;
+  for (int s = 0; s < a->n_seg; ++s) needs_mask = needs_mask || a->seg_text_valid[s] < a->seg_text_len[s];
+  p.needs_mask = needs_mask;
+  if (a->n_hist > 0 && a->cache) {
+    const int64_t rows = (int64_t)a->n_hist * a->cache->tokens_per_frame;
+    p.hist_tiles = (int32_t)((rows + 63) / 64);
+    p.hist_int8 = a->cache->dtype == SEGC_INT8;
+  }
+  if (n_cu <= 0 && device_cu_count(&n_cu)) return -1;
+  return segc::attn_split_plan(p, n_cu);
 }
 
 int segcausal_joint_attn_bwd(const segc_attn_bwd_args* a, void* stream) {

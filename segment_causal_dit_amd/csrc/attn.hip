@@ -112,6 +112,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
@@ -585,12 +586,25 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
 
-  // XCD-aware remap: hardware deals workgroup b to XCD b % 8; give each XCD a
-  // contiguous range of (head, query tile) in head-major order.
-  const int nwg = gridDim.x, b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3;
-  const int qn = nwg >> 3, rn = nwg & 7;
-  const int logical = (xcd < rn) ? xcd * (qn + 1) + local : rn * (qn + 1) + (xcd - rn) * qn + local;
+  // Workgroups [0, n_full) take whole (head, query tile)s, remapped XCD-aware:
+  // hardware deals workgroup b to XCD b % 8; each XCD gets a contiguous range
+  // in head-major order. Later workgroups (split > 1) take key range `part`
+  // of one of the remaining tiles.
+  const int b = blockIdx.x;
+  int logical, part = -1;
+  if (b < p.n_full) {
+    const int nwg = p.n_full;
+    const int xcd = b & 7, local = b >> 3;
+    const int qn = nwg >> 3, rn = nwg & 7;
+    logical = (xcd < rn) ? xcd * (qn + 1) + local : rn * (qn + 1) + (xcd - rn) * qn + local;
+  } else {
+    // range-major: the split workgroups in flight together (and those dealt to
+    // one XCD) cover few key ranges, so they share K/V in L2
+    const int rest = p.n_qtiles * p.n_heads - p.n_full;
+    const int idx = b - p.n_full;
+    part = idx / rest;
+    logical = p.n_full + (idx - part * rest);
+  }
   const int head = logical / p.n_qtiles;
   const int qtile = logical - head * p.n_qtiles;
 
@@ -606,6 +620,12 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     mw.kseg.s = 0;
   }
   const int n_tiles = p.hist_tiles + (cur_end + BN - 1) / BN;
+  // key tiles [tb, te) of this workgroup (a split covers one key range)
+  int tb = 0, te = n_tiles;
+  if (part >= 0) {
+    tb = (int)((int64_t)part * n_tiles / p.split);
+    te = (int)((int64_t)(part + 1) * n_tiles / p.split);
+  }
 
   // Q operands (B of S^T = K Q^T) and the query row's segment
   const int qrow = m0 + 32 * w + lr;
@@ -661,9 +681,11 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     // (a group then never straddles a frame); other tiles take the general path.
     const bool hwalk = p.G % RW == 0;
     const int full_hist_tiles = p.n_hist_rows / BN;
-    int hf = 0, hoff = RW * w, hslot = 0;
-    if (stager && hwalk && full_hist_tiles > 0) {
-      while (hoff >= p.G) { hoff -= p.G; ++hf; }
+    int hf = 0, hoff = 0, hslot = 0;
+    if (stager && hwalk && tb < full_hist_tiles) {
+      const int g0 = BN * tb + RW * w;
+      hf = g0 / p.G;
+      hoff = g0 - hf * p.G;
       hslot = const_load(p.hist_slots + hf);
     }
     auto issue = [&](int t, int slot) __attribute__((always_inline)) {
@@ -681,40 +703,42 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
       }
     };
     auto info_at = [&](int slot) __attribute__((always_inline)) { return (int*)(smem + PI_OFF + slot * INFO_BYTES); };
-    bool m0t = tile_masked<kSeg>(p, tile_at(p, 0, cur_end), mw);
+    // (a split workgroup starts at tile tb > 0 only without segment structure,
+    // whose mask walk is stateless)
+    bool m0t = tile_masked<kSeg>(p, tile_at(p, tb, cur_end), mw);
     const int s0 = mw.kseg.s;
-    bool m1t = n_tiles > 1 && tile_masked<kSeg>(p, tile_at(p, 1, cur_end), mw);
+    bool m1t = tb + 1 < te && tile_masked<kSeg>(p, tile_at(p, tb + 1, cur_end), mw);
     const int s1 = mw.kseg.s;
     if (stager) {
-      issue(0, 0);
-      if (n_tiles > 1) issue(1, 1);
+      issue(tb, 0);
+      if (tb + 1 < te) issue(tb + 1, 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (m0t) store_info<kSeg>(p, tile_at(p, 0, cur_end), tid, info_at(0), s0);
-      if (m1t) store_info<kSeg>(p, tile_at(p, 1, cur_end), tid, info_at(1), s1);
+      if (m0t) store_info<kSeg>(p, tile_at(p, tb, cur_end), tid, info_at(0), s0);
+      if (m1t) store_info<kSeg>(p, tile_at(p, tb + 1, cur_end), tid, info_at(1), s1);
     }
     __syncthreads();
-    const int n_pairs = (n_tiles + 1) >> 1;
+    const int n_pairs = (te - tb + 1) >> 1;
     // the loop body is instantiated once per slot parity, so that every LDS
     // operand address is a loop-invariant per-lane base plus an immediate
     auto pair_iter = [&](int u, int cs) __attribute__((always_inline)) {
       const int ns = 2 - cs;
       __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0) only
-      const int t0 = 2 * u;
+      const int t0 = tb + 2 * u;
       // The staging waves issue tile t0+2's loads after the first tile and
       // tile t0+3's between the second tile's S^T products and its softmax:
       // issued all at the start of the iteration (or right after the first
       // tile's S^T products) they held the staging waves back, and every
       // wave waits for those at the barrier.
       auto none = [&]() __attribute__((always_inline)) {};
-      auto second = [&]() __attribute__((always_inline)) { if (stager && t0 + 3 < n_tiles) issue(t0 + 3, ns + 1); };
+      auto second = [&]() __attribute__((always_inline)) { if (stager && t0 + 3 < te) issue(t0 + 3, ns + 1); };
       half(cs, m0t, none);
-      if (stager && t0 + 2 < n_tiles) issue(t0 + 2, ns);
-      if (t0 + 1 < n_tiles) half(cs + 1, m1t, second);
-      const bool n0 = t0 + 2 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t0 + 2, cur_end), mw);
+      if (stager && t0 + 2 < te) issue(t0 + 2, ns);
+      if (t0 + 1 < te) half(cs + 1, m1t, second);
+      const bool n0 = t0 + 2 < te && tile_masked<kSeg>(p, tile_at(p, t0 + 2, cur_end), mw);
       const int sg0 = mw.kseg.s;
-      const bool n1 = t0 + 3 < n_tiles && tile_masked<kSeg>(p, tile_at(p, t0 + 3, cur_end), mw);
+      const bool n1 = t0 + 3 < te && tile_masked<kSeg>(p, tile_at(p, t0 + 3, cur_end), mw);
       const int sg1 = mw.kseg.s;
-      if (stager && t0 + 2 < n_tiles) {
+      if (stager && t0 + 2 < te) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (n0) store_info<kSeg>(p, tile_at(p, t0 + 2, cur_end), tid, info_at(ns), sg0);
         if (n1) store_info<kSeg>(p, tile_at(p, t0 + 3, cur_end), tid, info_at(ns + 1), sg1);
@@ -777,8 +801,29 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     }
   }
 
-  // epilogue: O = acc / l, bf16; lse = m * sm_scale + ln l
   const float lt = xhalf_sum(rs.l);
+  if (part >= 0) {
+    // one key range of a split tile: unnormalised O, row max m and row sum l
+    if (qok) {
+      const int64_t rest = (int64_t)p.n_qtiles * p.n_heads - p.n_full;
+      const int64_t row = ((int64_t)(logical - p.n_full) * p.split + part) * BM + 32 * w + lr;
+      float* dst = p.ws + row * D + 4 * hh;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const f32x4 v4 = {o[db][4 * jq], o[db][4 * jq + 1], o[db][4 * jq + 2], o[db][4 * jq + 3]};
+          *(f32x4*)(dst + 32 * db + 8 * jq) = v4;
+        }
+      if (hh == 0) {
+        float* ml = p.ws + rest * p.split * BM * D + row * 2;
+        ml[0] = rs.m;
+        ml[1] = lt;
+      }
+    }
+    return;
+  }
+  // epilogue: O = acc / l, bf16; lse = m * sm_scale + ln l
   const float inv = 1.0f / lt;
   if (qok) {
     uint16_t* dst = p.o + (int64_t)qrow * p.o_st + head * p.o_sh + 4 * hh;
@@ -795,12 +840,87 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   }
 }
 
+// Merge the key ranges of the split tiles: for each row, M = max m_s,
+// O = sum_s 2^((m_s - M) c) O_s / sum_s 2^((m_s - M) c) l_s, lse = M sm_scale +
+// ln(that sum), as one workgroup would have produced (up to rounding order).
+// 32 lanes per row, 4 columns each; 8 rows per workgroup.
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  const int64_t rest = (int64_t)p.n_qtiles * p.n_heads - p.n_full;
+  const int64_t rg = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);   // row among the split tiles
+  const int r = (int)(rg / BM), rl = (int)(rg - (int64_t)r * BM);
+  if (r >= rest) return;
+  const int logical = p.n_full + r;
+  const int head = logical / p.n_qtiles;
+  const int qrow = (logical - head * p.n_qtiles) * BM + rl;
+  if (qrow >= p.n_cur) return;
+  const int c4 = 4 * (threadIdx.x & 31);
+  const float* ml = p.ws + rest * p.split * BM * D;
+  float mx = -INFINITY;
+  for (int k = 0; k < p.split; ++k) mx = fmaxf(mx, ml[(((int64_t)r * p.split + k) * BM + rl) * 2]);
+  float l = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < p.split; ++k) {
+    const int64_t row = ((int64_t)r * p.split + k) * BM + rl;
+    const float m = ml[row * 2];
+    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((m - mx) * p.scale_log2);
+    l += f * ml[row * 2 + 1];
+    const f32x4 v = *(const f32x4*)(p.ws + row * D + c4);
+    acc += f * v;
+  }
+  const float inv = 1.0f / l;
+  const u32x2 v2 = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+  *(u32x2*)(p.o + (int64_t)qrow * p.o_st + head * p.o_sh + c4) = v2;
+  if (p.lse && c4 == 0) p.lse[(int64_t)head * p.n_cur + qrow] = mx * p.sm_scale + logf(l);
+}
+
 }  // namespace
+
+int64_t attn_split_plan(AttnParams& p, int n_cu) {
+  p.n_qtiles = (p.n_cur + BM - 1) / BM;
+  const int64_t nwg = (int64_t)p.n_qtiles * p.n_heads;
+  p.n_full = (int32_t)nwg;
+  p.split = 1;
+  // only the two-tile kernel without segment structure splits: its tiles
+  // are independent of where a key range starts
+  const bool pair = !(p.hist_tiles > 0 && p.hist_int8);
+  if (p.needs_mask || !pair || n_cu <= 0 || nwg < 1) return 0;
+  const int64_t full = nwg / n_cu * n_cu, rest = nwg - full;
+  // Only long launches split: measured on MI355X, a split of launches of one
+  // or two rounds (c2, c3) cost more than it saved, and at c4 (15.6 rounds)
+  // it saves about 1 %, well under the idle share of the last round (the
+  // clock rises while part of the chip idles, which makes that round cheaper).
+  if (rest == 0 || full < 4 * (int64_t)n_cu) return 0;
+  const int n_tiles = p.hist_tiles + (p.n_cur + BN - 1) / BN;
+  // Cost model: a workgroup takes about 1.7 us per 64-key tile; splitting the
+  // last round into s ranges shortens it from one workgroup time to
+  // ceil(rest s / n_cu) / s of one, and costs the partial results written and
+  // read again (2 x 130 KiB per split workgroup at about 5 TB/s) plus one more
+  // launch (about 10 us). At most 8 ranges per tile (16 measured no better).
+  const double t_wg = 1.7 * n_tiles;
+  double best_gain = 0.0;
+  int best = 1;
+  for (int sp = 2; sp <= 8 && 4 * sp <= n_tiles; ++sp) {
+    const double last = (double)((rest * sp + n_cu - 1) / n_cu) / sp;
+    const double gain = (1.0 - last) * t_wg - (double)rest * sp * 2.0 * BM * (D + 2) * 4 / 5.0e6 - 10.0;
+    if (gain > best_gain) {
+      best_gain = gain;
+      best = sp;
+    }
+  }
+  if (best == 1) return 0;
+  p.n_full = (int32_t)full;
+  p.split = best;
+  return rest * best * (int64_t)BM * (D + 2) * 4;
+}
 
 hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
   AttnParams p = p0;
   p.n_qtiles = (p.n_cur + BM - 1) / BM;
-  const int64_t nwg = (int64_t)p.n_qtiles * p.n_heads;
+  if (p.split <= 1) {
+    p.split = 1;
+    p.n_full = (int32_t)((int64_t)p.n_qtiles * p.n_heads);
+  }
+  const int64_t nwg = p.n_full + ((int64_t)p.n_qtiles * p.n_heads - p.n_full) * p.split;
   // more than 64 KB of dynamic LDS must be allowed explicitly (gfx950 has 160 KB per CU)
   const bool pair = !(p.hist_tiles > 0 && p.hist_int8);
   const void* fn = p.needs_mask ? (pair ? (const void*)attn_kernel<true, true> : (const void*)attn_kernel<true, false>)
@@ -815,6 +935,12 @@ hipError_t launch_attn(const AttnParams& p0, hipStream_t s) {
   } else {
     if (pair) hipLaunchKernelGGL((attn_kernel<false, true>), grid, block, lds, s, p);
     else hipLaunchKernelGGL((attn_kernel<false, false>), grid, block, lds, s, p);
+  }
+  if (p.split > 1) {
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = ((int64_t)p.n_qtiles * p.n_heads - p.n_full) * BM;
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -84,7 +84,16 @@ struct AttnParams {
   int32_t seg_start[kMaxSeg + 1];
   int32_t seg_text_len[kMaxSeg];
   int32_t seg_text_valid[kMaxSeg];
+  // Split of the last partial round (split > 1): workgroups [0, n_full) take
+  // whole (head, query tile)s; each later tile is taken by `split` workgroups
+  // over key ranges, whose partial results go to ws and are merged after.
+  int32_t n_full;
+  int32_t split;
+  float* ws;
 };
+// Workspace bytes and split for p on a device with n_cu compute units (fills
+// n_full and split in p; split = 1 and 0 bytes when the call does not split).
+int64_t attn_split_plan(AttnParams& p, int n_cu);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 
 // Gradients of the packed form (no history): delta = rowsum(do * o), then

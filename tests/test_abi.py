@@ -22,7 +22,7 @@ FAKE = 0x10000000          # a 16-byte aligned stand-in pointer: never dereferen
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
 
 
 def test_exports_every_declared_symbol():
@@ -174,6 +174,8 @@ def _attn(segs=((0, 16, 16),), n_cur=None, **kw):
     (dict(n_hist=9, cache=_cache(n_heads=2), hist_slots=FAKE), 1),  # more frames than slots
     (dict(n_hist=2, cache=_cache(), hist_slots=FAKE), 1),           # head count mismatch
     (dict(n_hist=2, cache=_cache(n_heads=2, head_dim=64), hist_slots=FAKE), 2),
+    (dict(reserved=1), 1), (dict(reserved2=1), 1), (dict(workspace_bytes=-1), 1),
+    (dict(workspace=FAKE + 8, workspace_bytes=1 << 20), 1),         # workspace not 16-byte aligned
 ])
 def test_attn_rejects(kw, code):
     assert _attn(**kw) == code
@@ -197,6 +199,41 @@ def test_attn_rejects_bad_segments(segs, n_cur):
         assert lib.segcausal_joint_attn(ctypes.byref(a), None) == 1
         return
     assert _attn(segs=segs, n_cur=n_cur) == 1
+
+
+def _ws_bytes(n_cur, n_heads, segs, n_hist=0, cache=None, n_cu=256):
+    starts = [sg[0] for sg in segs] + [n_cur]
+    a = sc.SegcAttnArgs()
+    a.n_cur, a.n_heads, a.head_dim, a.n_seg = n_cur, n_heads, 128, len(segs)
+    a.seg_start = (ctypes.c_int32 * len(starts))(*starts)
+    a.seg_text_len = (ctypes.c_int32 * len(segs))(*[sg[1] for sg in segs])
+    a.seg_text_valid = (ctypes.c_int32 * len(segs))(*[sg[2] for sg in segs])
+    a.n_hist = n_hist
+    if cache is not None:
+        a.cache = ctypes.pointer(cache)
+    return lib.segcausal_joint_attn_workspace_bytes(ctypes.byref(a), n_cu)
+
+
+def test_attn_workspace_bytes_split_plan():
+    # c4: 249 query tiles x 16 heads = 3,984 workgroups on 256 compute units:
+    # the last 144 tiles split 7 ways (the cost model's pick), each split
+    # keeping an fp32 256 x 128 O and 256 (max, sum) pairs
+    seg = [(0, 256, 256)]
+    bf16_360 = _cache(dtype=0, n_slots=360, tokens_per_frame=880)
+    c4 = dict(n_cur=63616, n_heads=16, segs=seg, n_hist=288)
+    assert _ws_bytes(cache=bf16_360, **c4) == 144 * 7 * 256 * 130 * 4
+    # the same history held as INT8 (one-tile schedule) and a segment structure never split
+    assert _ws_bytes(cache=_cache(dtype=1, n_slots=360, tokens_per_frame=880), **c4) == 0
+    assert _ws_bytes(63616, 16, [(0, 256, 200)], 288, bf16_360) == 0
+    assert _ws_bytes(63616, 16, [(0, 256, 256), (32000, 256, 256)], 288, bf16_360) == 0
+    # a whole number of rounds, or fewer than 4 whole rounds (c1, c2: they measured slower split)
+    assert _ws_bytes(256 * 16, 16, seg, 288, bf16_360) == 0
+    assert _ws_bytes(7296, 16, seg) == 0
+    assert _ws_bytes(7296, 16, seg, 18, bf16_360) == 0
+    # 65 query tiles x 16 heads: 4 rounds + 16 tiles, split 8 ways
+    assert _ws_bytes(65 * 256, 16, seg, 20, bf16_360) == 16 * 8 * 256 * 130 * 4
+    assert _ws_bytes(65 * 256, 16, seg, 20, bf16_360, n_cu=1040) == 0
+    assert lib.segcausal_joint_attn_workspace_bytes(None, 256) == -1
 
 
 def test_attn_noop_and_null_args():

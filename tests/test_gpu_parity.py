@@ -403,9 +403,11 @@ def test_attention_over_dequantised_window_is_bit_identical(name):
     r = gpu_chain(inp, with_lse=True)
     win = _dequant_window(r.cache, r.slots)
     lse = torch.empty_like(r.lse)
+    # without a workspace neither path splits its last round, so the two are
+    # the same arithmetic on the same bf16 operands
     o = sc.segcausal_joint_attn(r.q, r.k, r.v, inp.segments, inp.cfg.sm_scale, cache=win,
                                 hist_slots=torch.arange(len(r.slots), dtype=torch.int32, device="cuda"),
-                                lse=lse)
+                                lse=lse, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(o, r.o)
     assert torch.equal(lse, r.lse)
@@ -466,20 +468,100 @@ def test_c4_append_and_rope_bit_exact():
     # the BF16-window form of the same attention is bit-identical
     import torch
     win = _dequant_window(r.cache, r.slots)
+    win_slots = torch.arange(len(r.slots), dtype=torch.int32, device="cuda")
     o2 = sc.segcausal_joint_attn(r.q, r.k, r.v, inp.segments, cfg.sm_scale, cache=win,
-                                 hist_slots=torch.arange(len(r.slots), dtype=torch.int32, device="cuda"))
+                                 hist_slots=win_slots, workspace=None)
     torch.cuda.synchronize()
     assert torch.equal(o2, r.o)
+    # the BF16-window form with its last round split by key range (the bench's
+    # launch): checked against the oracle below and against the unsplit form
+    assert sc.attn_workspace_bytes(cfg.n_cur, cfg.n_heads, inp.segments, len(r.slots), win) > 0
+    lse3 = torch.empty_like(r.lse)
+    o3 = sc.segcausal_joint_attn(r.q, r.k, r.v, inp.segments, cfg.sm_scale, cache=win,
+                                 hist_slots=win_slots, lse=lse3)
+    torch.cuda.synchronize()
+    e_split = attn_errors(to_f64(o3), to_f64(o2))
+    _say("  c4 split vs unsplit: %r" % (e_split,))
+    assert e_split.ok(), e_split
     del win, o2
     # attention on sampled rows, reading the cache exactly as the oracle builds it
     rows = np.concatenate([np.arange(0, 256, 4), 256 + rng.choice(cfg.n_video, 192, replace=False)])
     _say("c4 oracle rows", len(rows))
     o_ref, lse_ref = _c4_rows_oracle(inp, rows)
-    got = to_f64(r.o[torch.from_numpy(rows).cuda()])
-    e = attn_errors(got, o_ref)
-    lerr = float(np.abs(r.lse.cpu().numpy()[:, rows] - lse_ref).max())
-    _say("  c4 sampled: %r lse %.3e" % (e, lerr))
+    ridx = torch.from_numpy(rows).cuda()
+    for name, o, lse in (("int8 cache", r.o, r.lse), ("split window", o3, lse3)):
+        got = to_f64(o[ridx])
+        e = attn_errors(got, o_ref)
+        lerr = float(np.abs(lse.cpu().numpy()[:, rows] - lse_ref).max())
+        _say("  c4 sampled, %s: %r lse %.3e" % (name, e, lerr))
+        assert e.ok() and lerr <= LSE_ERR, (name, e, lerr)
+
+
+def test_split_last_round_bf16_history():
+    """65 query tiles x 16 heads = 1,040 workgroups on 256 compute units: the
+    last 16 tiles (head 15's last 16) are split by key range over a 20-frame
+    BF16 history in permuted slots plus the current rows. Checked against the
+    oracle on rows of the split tiles and against the unsplit launch
+    everywhere."""
+    import torch
+    g, h, nf, n_slots = 880, 16, 20, 24
+    n_cur = 65 * 256
+    segs = [(0, 256, 256)]
+    qb = workloads.normal_bf16(71, (n_cur, h, HEAD_DIM), 128 ** -0.5)
+    kb = workloads.normal_bf16(72, (n_cur, h, HEAD_DIM))
+    vb = workloads.normal_bf16(73, (n_cur, h, HEAD_DIM))
+    hkb = workloads.normal_bf16(74, (n_slots, h, g, HEAD_DIM))
+    hvb = workloads.normal_bf16(75, (n_slots, h, g, HEAD_DIM))
+    cache = sc.KVCache(n_slots, h, g, "bf16", "cuda")
+    cache.k.copy_(_bf(hkb).view(cache.k.shape))
+    cache.v.copy_(_bf(hvb).view(cache.v.shape))
+    slots = np.random.default_rng(76).permutation(n_slots)[:nf].astype(np.int32)
+    hs = torch.from_numpy(slots).cuda()
+    need = sc.attn_workspace_bytes(n_cur, h, segs, nf, cache)
+    _say("split workspace bytes", need)
+    assert need > 0
+    q, k, v = _bf(qb), _bf(kb), _bf(vb)
+    lse_s = torch.empty((h, n_cur), dtype=torch.float32, device="cuda")
+    lse_p = torch.empty_like(lse_s)
+    o_s = sc.segcausal_joint_attn(q, k, v, segs, 1.0, cache=cache, hist_slots=hs, lse=lse_s)
+    o_p = sc.segcausal_joint_attn(q, k, v, segs, 1.0, cache=cache, hist_slots=hs, lse=lse_p,
+                                  workspace=None)
+    torch.cuda.synchronize()
+    e = attn_errors(to_f64(o_s), to_f64(o_p))
+    _say("  split vs unsplit: %r" % (e,))
+    assert e.ok(), e
+    assert float((lse_s - lse_p).abs().max()) <= LSE_ERR
+    # rows of the split tiles (head 15's last 16 query tiles: rows from 49 * 256)
+    # and of whole tiles, against the oracle
+    rng = np.random.default_rng(77)
+    rows = np.sort(np.concatenate([[0, 255, 49 * 256, 49 * 256 + 1, n_cur - 1],
+                                   rng.choice(np.arange(49 * 256, n_cur), 40, replace=False)]))
+    hk = np.stack([oracle.bf16_bits_to_f64(hkb[s]) for s in slots])            # [nf, H, G, D]
+    hv = np.stack([oracle.bf16_bits_to_f64(hvb[s]) for s in slots])
+    hk = hk.transpose(0, 2, 1, 3).reshape(nf * g, h, HEAD_DIM)
+    hv = hv.transpose(0, 2, 1, 3).reshape(nf * g, h, HEAD_DIM)
+    o_ref, lse_ref = oracle.joint_attn_rows(*(oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb)),
+                                            [oracle.Segment(*s) for s in segs], rows, hk, hv, 1.0)
+    ridx = torch.from_numpy(rows).cuda()
+    e = attn_errors(to_f64(o_s[ridx]), o_ref)
+    lerr = float(np.abs(lse_s.cpu().numpy()[:, rows] - lse_ref).max())
+    _say("  split rows vs oracle: %r lse %.3e" % (e, lerr))
     assert e.ok() and lerr <= LSE_ERR, (e, lerr)
+
+
+def test_split_workspace_refused_when_too_small():
+    import torch
+    g, h = 880, 16
+    n_cur = 65 * 256
+    segs = [(0, 256, 256)]
+    cache = sc.KVCache(8, h, g, "bf16", "cuda")
+    need = sc.attn_workspace_bytes(n_cur, h, segs, 8, cache)
+    assert need > 0
+    x = torch.zeros((n_cur, h, HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    hs = torch.arange(8, dtype=torch.int32, device="cuda")
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sc.SegcError):
+        sc.segcausal_joint_attn(x, x, x, segs, 1.0, cache=cache, hist_slots=hs, workspace=small)
 
 
 def _c4_rows_oracle(inp, rows):
