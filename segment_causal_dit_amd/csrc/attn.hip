@@ -592,7 +592,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   // of one of the remaining tiles.
   const int b = blockIdx.x;
   int logical, part = -1;
-  if (b < p.n_full) {
+  if (kSeg || !kPair || b < p.n_full) {     // only the single-segment two-tile kernel splits
     const int nwg = p.n_full;
     const int xcd = b & 7, local = b >> 3;
     const int qn = nwg >> 3, rn = nwg & 7;
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
   const int n_tiles = p.hist_tiles + (cur_end + BN - 1) / BN;
   // key tiles [tb, te) of this workgroup (a split covers one key range)
   int tb = 0, te = n_tiles;
-  if (part >= 0) {
+  if (!kSeg && kPair && part >= 0) {
     tb = (int)((int64_t)part * n_tiles / p.split);
     te = (int)((int64_t)(part + 1) * n_tiles / p.split);
   }

@@ -545,16 +545,29 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
     }
     const float* tb = (const float*)(cur + TOFF);
     f32x16 pm, ds;
+    // exponent arguments; a tile that needs the mask sends invisible pairs to -inf
+    float arg[16];
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
-      const int r = 32 * qh + 8 * jq + 4 * hh;       // tile rows r .. r + 3
-      const f32x4 l4 = *(const f32x4*)(tb + r);
-      const f32x4 d4 = *(const f32x4*)(tb + BN + r);
-      const i32x4 g4 = *(const i32x4*)((const int*)tb + 2 * BN + r);
+      const f32x4 l4 = *(const f32x4*)(tb + 32 * qh + 8 * jq + 4 * hh);   // tile rows r .. r + 3
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) arg[4 * jq + jj] = fmaf(s[4 * jq + jj], c, -l4[jj]);
+    }
+    if (masked) {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const i32x4 g4 = *(const i32x4*)((const int*)tb + 2 * BN + 32 * qh + 8 * jq + 4 * hh);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (g4[jj] < klo || g4[jj] > khi) arg[4 * jq + jj] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const f32x4 d4 = *(const f32x4*)(tb + BN + 32 * qh + 8 * jq + 4 * hh);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const bool vis = !masked || (g4[jj] >= klo && g4[jj] <= khi);
-        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[4 * jq + jj], c, -l4[jj])) : 0.0f;
+        const float pr = __builtin_amdgcn_exp2f(arg[4 * jq + jj]);
         pm[4 * jq + jj] = pr;
         ds[4 * jq + jj] = pr * (dp[4 * jq + jj] - d4[jj]);
       }
