@@ -31,8 +31,9 @@
 //    their partial dK and dV through LDS at the end.
 // 64-row tiles are staged through LDS, double buffered, by direct global->LDS
 // loads issued from inline assembly and awaited explicitly once per tile (the
-// dK/dV kernel issues the next tile's loads after the current tile's S and dP
-// products, and fetches its lse and delta in the same place).
+// dK/dV kernel issues the next tile's loads after six of the eight steps of
+// the current tile's S and dP products, and fetches its lse and delta in the
+// same place). Both kernels order their workgroups XCD-aware and head-major.
 // Chunk c of tile row r sits at c ^ (((r & 3) << 2) | ((r >> 2) & 3)): every
 // read by rows (16 consecutive rows, one chunk) and every transposing read
 // (4 aligned chunks of 4 aligned rows) touches distinct bank groups. Tile
@@ -88,6 +89,15 @@ __device__ inline int seg_of(const AttnBwdParams& p, int r) {
   int s = 0;
   for (int i = 1; i < p.n_seg; ++i) s += (r >= p.seg_start[i]) ? 1 : 0;
   return s;
+}
+
+// Logical index of this workgroup in a launch of nwg: workgroup b runs on XCD
+// b % 8, and each XCD gets a contiguous range (the first nwg % 8 XCDs one
+// more), so the workgroups resident on one XCD take neighbouring indices.
+__device__ inline int xcd_head_major(int nwg) {
+  const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
+  const int qn = nwg >> 3, rn = nwg & 7;
+  return (xcd < rn) ? xcd * (qn + 1) + local : rn * (qn + 1) + (xcd - rn) * qn + local;
 }
 
 // no text row (valid or padded) in [a, b)
@@ -263,11 +273,15 @@ __global__ __launch_bounds__(QT, 2) void dq_kernel(AttnBwdParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, hh = lane >> 5;
-  // heaviest query tiles (the last ones see the most keys) first
+  // Workgroup b runs on XCD b % 8; each XCD takes a contiguous head-major
+  // range, so the workgroups resident on one XCD walk the same head's key
+  // tiles and share them in its L2. Inside a head the heaviest query tiles
+  // (the last ones see the most keys) go first.
   const int nwg = gridDim.x;
-  const int logical = nwg - 1 - (int)blockIdx.x;
-  const int qtile = logical / p.n_heads;
-  const int head = logical - qtile * p.n_heads;
+  const int n_qt = nwg / p.n_heads;
+  const int logical = xcd_head_major(nwg);
+  const int head = logical / n_qt;
+  const int qtile = n_qt - 1 - (logical - head * n_qt);
 
   const int m0 = qtile * QBM;
   const int wg_last = min(m0 + QBM, p.n) - 1;
@@ -439,9 +453,13 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = w & 3, qh = w >> 2;
   const int lr = lane & 31, hh = lane >> 5;
-  // the first key tiles are seen by the most queries: they go first
-  const int ktile = blockIdx.x / p.n_heads;
-  const int head = blockIdx.x - ktile * p.n_heads;
+  // XCD-aware head-major order as in the dQ kernel; inside a head the first
+  // key tiles, seen by the most queries, go first
+  const int nwg = gridDim.x;
+  const int n_kt = nwg / p.n_heads;
+  const int logical = xcd_head_major(nwg);
+  const int head = logical / n_kt;
+  const int ktile = logical - head * n_kt;
 
   const int j0 = ktile * KBN;
   const int j1 = min(j0 + KBN, p.n);
@@ -535,13 +553,15 @@ __global__ __launch_bounds__(KT, 2) void dkdv_kernel(AttnBwdParams p) {
       const bf16x8 bv = *(const bf16x8*)(vtile_l + t_off(lr, 2 * dt + hh));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, bv, dp, 0, 0, 0);
-    }
-    // the next tile's loads go out after this tile's S and dP products (at
-    // the start of the iteration, or later, they measured slower)
-    if (has_next) {
-      stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt + AOFF,
-                          nxt + BOFF);
-      fetch_next(q0 + BN);
+      // the next tile's loads go out after six of the eight steps: their
+      // writes into LDS then land after the products' operand reads, which
+      // keep the LDS busy (issued at the start of the iteration they
+      // measured 7 % slower)
+      if (dt == 5 && has_next) {
+        stage_pair<BN / KW>(qb, p.q_st, db_, p.do_st, q0 + BN, min(BN, p.n - q0 - BN), w, lane, nxt + AOFF,
+                            nxt + BOFF);
+        fetch_next(q0 + BN);
+      }
     }
     const float* tb = (const float*)(cur + TOFF);
     f32x16 pm, ds;
