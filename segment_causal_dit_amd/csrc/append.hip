@@ -90,7 +90,7 @@ __device__ inline u32x2 quant_row8(const u32x4 in, float* scale_out) {
   }
   // biased byte written in place, then XOR 0x80 per byte gives the
   // two's-complement code
-  u32x2 out;
+  uint32_t out[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     uint32_t wd = 0;
@@ -98,7 +98,7 @@ __device__ inline u32x2 quant_row8(const u32x4 in, float* scale_out) {
     for (int j = 0; j < 4; ++j) wd = __builtin_amdgcn_cvt_pk_u8_f32(v[4 * h + j], j, wd);
     out[h] = wd ^ 0x80808080u;
   }
-  return out;
+  return u32x2{out[0], out[1]};
 }
 
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendParams p) {

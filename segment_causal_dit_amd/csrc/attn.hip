@@ -831,9 +831,8 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
-        u32x2 v2;
-        v2.x = pack_bf16(o[db][4 * jq] * inv, o[db][4 * jq + 1] * inv);
-        v2.y = pack_bf16(o[db][4 * jq + 2] * inv, o[db][4 * jq + 3] * inv);
+        const u32x2 v2 = {pack_bf16(o[db][4 * jq] * inv, o[db][4 * jq + 1] * inv),
+                          pack_bf16(o[db][4 * jq + 2] * inv, o[db][4 * jq + 3] * inv)};
         *(u32x2*)(dst + 32 * db + 8 * jq) = v2;
       }
     if (p.lse && hh == 0) p.lse[(int64_t)head * p.n_cur + qrow] = rs.m * p.sm_scale + logf(lt);

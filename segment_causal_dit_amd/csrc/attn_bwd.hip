@@ -235,9 +235,8 @@ __device__ inline void store_row(uint16_t* row, int hh, const f32x16 (&x)[4], fl
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
-      u32x2 v2;
-      v2.x = pack_bf16(x[db][4 * jq] * scale, x[db][4 * jq + 1] * scale);
-      v2.y = pack_bf16(x[db][4 * jq + 2] * scale, x[db][4 * jq + 3] * scale);
+      const u32x2 v2 = {pack_bf16(x[db][4 * jq] * scale, x[db][4 * jq + 1] * scale),
+                        pack_bf16(x[db][4 * jq + 2] * scale, x[db][4 * jq + 3] * scale)};
       *(u32x2*)(dst + 32 * db + 8 * jq) = v2;
     }
 }

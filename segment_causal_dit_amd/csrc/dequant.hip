@@ -43,22 +43,16 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantParams p) {
   const int8_t* codes = isv ? p.cv : p.ck;
   const float s = (isv ? p.cvs : p.cks)[src];
   const u32x4 w = *(const u32x4*)(codes + src * 128 + 16 * part);
-  u32x4 lo, hi;
+  // packed pairs in a plain array, moved into the stored vectors in one piece
+  uint32_t pr[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t pr0 = pack_bf16(dq(w[e], 0, s), dq(w[e], 1, s));
-    const uint32_t pr1 = pack_bf16(dq(w[e], 2, s), dq(w[e], 3, s));
-    if (e < 2) {
-      lo[2 * e] = pr0;
-      lo[2 * e + 1] = pr1;
-    } else {
-      hi[2 * (e - 2)] = pr0;
-      hi[2 * (e - 2) + 1] = pr1;
-    }
+    pr[2 * e] = pack_bf16(dq(w[e], 0, s), dq(w[e], 1, s));
+    pr[2 * e + 1] = pack_bf16(dq(w[e], 2, s), dq(w[e], 3, s));
   }
   uint16_t* out = (isv ? p.ov : p.ok) + (int64_t)row * 128 + 16 * part;
-  *(u32x4*)out = lo;
-  *(u32x4*)(out + 8) = hi;
+  *(u32x4*)out = u32x4{pr[0], pr[1], pr[2], pr[3]};
+  *(u32x4*)(out + 8) = u32x4{pr[4], pr[5], pr[6], pr[7]};
 }
 
 }  // namespace

@@ -62,10 +62,8 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 
 // Four signed codes (one dword) -> four bf16, exact.
 __device__ inline u32x2 codes_to_bf16(uint32_t d) {
-  u32x2 r;
-  r.x = pack_bf16((float)(int8_t)(d & 0xFF), (float)(int8_t)((d >> 8) & 0xFF));
-  r.y = pack_bf16((float)(int8_t)((d >> 16) & 0xFF), (float)(int8_t)(d >> 24));
-  return r;
+  return u32x2{pack_bf16((float)(int8_t)(d & 0xFF), (float)(int8_t)((d >> 8) & 0xFF)),
+               pack_bf16((float)(int8_t)((d >> 16) & 0xFF), (float)(int8_t)(d >> 24))};
 }
 
 // 16 codes per thread -> 16 bf16 in the dense [n][k] workspace.
@@ -230,9 +228,8 @@ __global__ __launch_bounds__(NTH, 2) void w8a16_kernel(W8GemmParams p) {
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
           const f32x16& v = acc[nb][mb];
-          u32x2 o;
-          o.x = pack_bf16(fmaf(v[4 * jq], sc[jq][0], bi[jq][0]), fmaf(v[4 * jq + 1], sc[jq][1], bi[jq][1]));
-          o.y = pack_bf16(fmaf(v[4 * jq + 2], sc[jq][2], bi[jq][2]), fmaf(v[4 * jq + 3], sc[jq][3], bi[jq][3]));
+          const u32x2 o = {pack_bf16(fmaf(v[4 * jq], sc[jq][0], bi[jq][0]), fmaf(v[4 * jq + 1], sc[jq][1], bi[jq][1])),
+                           pack_bf16(fmaf(v[4 * jq + 2], sc[jq][2], bi[jq][2]), fmaf(v[4 * jq + 3], sc[jq][3], bi[jq][3]))};
           *(u32x2*)(dst + 8 * jq) = o;
         }
       }

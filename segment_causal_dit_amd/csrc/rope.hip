@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeParams p) {
     if (tok >= p.n_tok) break;
     const int64_t off = tok * p.stride_tok + (int64_t)head * p.stride_head + d8 * 8;
     const u32x4 in = *(const u32x4*)(p.x_in + off);
-    u32x4 out;
+    uint32_t out[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int pr = d8 * 4 + e;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void rope3d_kernel(RopeParams p) {
       }
       out[e] = w;
     }
-    *(u32x4*)(p.x_out + off) = out;
+    *(u32x4*)(p.x_out + off) = u32x4{out[0], out[1], out[2], out[3]};
   }
 }
 
