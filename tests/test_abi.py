@@ -233,6 +233,10 @@ def test_attn_workspace_bytes_split_plan():
     # 65 query tiles x 16 heads: 4 rounds + 16 tiles, split 8 ways
     assert _ws_bytes(65 * 256, 16, seg, 20, bf16_360) == 16 * 8 * 256 * 130 * 4
     assert _ws_bytes(65 * 256, 16, seg, 20, bf16_360, n_cu=1040) == 0
+    # the GPU split tests' shapes: 96, 188 and 56 remaining tiles in 5, 4 and 4 ranges
+    assert _ws_bytes(70 * 256 - 100, 16, seg) == 96 * 5 * 256 * 130 * 4
+    assert _ws_bytes(100 * 256 + 37, 12, seg, 4, _cache(dtype=0, n_slots=6, tokens_per_frame=880)) == 188 * 4 * 256 * 130 * 4
+    assert _ws_bytes(135 * 256, 8, seg, 10, _cache(dtype=0, n_slots=12, tokens_per_frame=880)) == 56 * 4 * 256 * 130 * 4
     assert lib.segcausal_joint_attn_workspace_bytes(None, 256) == -1
 
 

@@ -549,6 +549,72 @@ def test_split_last_round_bf16_history():
     assert e.ok() and lerr <= LSE_ERR, (e, lerr)
 
 
+@pytest.mark.parametrize("h,n_cur,nf", [
+    (16, 70 * 256 - 100, 0),      # no history, ragged last query tile
+    (12, 100 * 256 + 37, 4),      # 12 heads, 188 remaining tiles, ragged tail
+    (8, 135 * 256, 10),           # 8 heads, 56 remaining tiles
+])
+def test_split_matches_unsplit_across_shapes(h, n_cur, nf):
+    """Launches of at least four whole rounds with a partial last round, over
+    a BF16 history (or none): the split launch (key ranges of the last
+    round's tiles merged by lse) against the unsplit one, everywhere, and a
+    sample of rows of the split tiles against the oracle."""
+    import torch
+    g, n_slots = 880, max(nf, 1) + 2
+    segs = [(0, 256, 256)]
+    seed = 80 + h
+    qb = workloads.normal_bf16(seed, (n_cur, h, HEAD_DIM), 128 ** -0.5)
+    kb = workloads.normal_bf16(seed + 1, (n_cur, h, HEAD_DIM))
+    vb = workloads.normal_bf16(seed + 2, (n_cur, h, HEAD_DIM))
+    q, k, v = _bf(qb), _bf(kb), _bf(vb)
+    cache = hs = None
+    hk = hv = None
+    if nf:
+        hkb = workloads.normal_bf16(seed + 3, (n_slots, h, g, HEAD_DIM))
+        hvb = workloads.normal_bf16(seed + 4, (n_slots, h, g, HEAD_DIM))
+        cache = sc.KVCache(n_slots, h, g, "bf16", "cuda")
+        cache.k.copy_(_bf(hkb).view(cache.k.shape))
+        cache.v.copy_(_bf(hvb).view(cache.v.shape))
+        slots = np.random.default_rng(seed + 5).permutation(n_slots)[:nf].astype(np.int32)
+        hs = torch.from_numpy(slots).cuda()
+        hk = np.stack([oracle.bf16_bits_to_f64(hkb[s_]) for s_ in slots]).transpose(0, 2, 1, 3)
+        hv = np.stack([oracle.bf16_bits_to_f64(hvb[s_]) for s_ in slots]).transpose(0, 2, 1, 3)
+        hk = hk.reshape(nf * g, h, HEAD_DIM)
+        hv = hv.reshape(nf * g, h, HEAD_DIM)
+    n_qt = (n_cur + 255) // 256
+    rest = n_qt * h - (n_qt * h) // 256 * 256
+    need = sc.attn_workspace_bytes(n_cur, h, segs, nf, cache)
+    split = need // (rest * 256 * (HEAD_DIM + 2) * 4) if need else 1
+    _say("split case h=%d n_cur=%d nf=%d: %d remaining tiles in %d ranges" % (h, n_cur, nf, rest, split))
+    assert need > 0 and 2 <= split <= 8
+    lse_s = torch.empty((h, n_cur), dtype=torch.float32, device="cuda")
+    lse_p = torch.empty_like(lse_s)
+    kw = dict(cache=cache, hist_slots=hs) if nf else {}
+    o_s = sc.segcausal_joint_attn(q, k, v, segs, 1.0, lse=lse_s, **kw)
+    o_p = sc.segcausal_joint_attn(q, k, v, segs, 1.0, lse=lse_p, workspace=None, **kw)
+    torch.cuda.synchronize()
+    e = attn_errors(to_f64(o_s), to_f64(o_p))
+    _say("  split vs unsplit: %r" % (e,))
+    assert e.ok(), e
+    assert float((lse_s - lse_p).abs().max()) <= LSE_ERR
+    # the split tiles are the last `rest` logical tiles: the last heads' last query tiles
+    first_split = n_qt * h - rest
+    rows = []
+    rng = np.random.default_rng(seed + 6)
+    for t in rng.choice(np.arange(first_split, n_qt * h), 6, replace=False):
+        qt = int(t) % n_qt
+        lo, hi = qt * 256, min(qt * 256 + 256, n_cur)
+        rows += [lo, hi - 1, int(rng.integers(lo, hi))]
+    rows = np.unique(np.array(rows))
+    o_ref, lse_ref = oracle.joint_attn_rows(*(oracle.bf16_bits_to_f64(x) for x in (qb, kb, vb)),
+                                            [oracle.Segment(*s_) for s_ in segs], rows, hk, hv, 1.0)
+    ridx = torch.from_numpy(rows).cuda()
+    e = attn_errors(to_f64(o_s[ridx]), o_ref)
+    lerr = float(np.abs(lse_s.cpu().numpy()[:, rows] - lse_ref).max())
+    _say("  split rows vs oracle: %r lse %.3e" % (e, lerr))
+    assert e.ok() and lerr <= LSE_ERR, (e, lerr)
+
+
 def test_split_workspace_refused_when_too_small():
     import torch
     g, h = 880, 16
